@@ -1,0 +1,363 @@
+"""Oracle for one single-stream DiT block, its ops, and one denoise step.
+
+Sources (page title, section):
+  [FlagOS]   "Qwen-Image-2.1 W8A8 - FlagOS for Mac", Quantization and validation
+  [mere]     "Qwen Image 2.1 native qualification", Numerical checks
+  [CoreAI]   "RGBA-Image-2.1 - Core AI port of Qwen-Image-2.1", intro and Graph contracts
+  [MNN]      "qwen-image-mnn" package description, What runs where / Install, run
+  [Paiton]   "Qwen_Image-2.1-MXFP4-Paiton", Runtime precision and quality / Tested operating limits
+
+Where the pages leave a step open, the reading taken is stated at the function.
+
+Precision modes of ``block_forward``:
+  "f32":  every value kept in fp64 (the reference for a GPU that computes in fp32).
+  "bf16": fp64 arithmetic, with each tensor the block stores rounded to bf16 at the
+          point where it is stored (activations, linear outputs, q/k/v, attention
+          output, GELU output, residual stream); statistics, softmax, accumulators and
+          modulation stay fp64.
+  "w8a8": "bf16" with the inputs of the four linears quantized to int8 per token and
+          the weights int8 per output channel (int32-exact accumulation).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "round_bf16", "quantize_rows", "int8_matmul_exact", "w8a8_linear", "linear",
+    "adaln_modulate", "qk_rmsnorm", "apply_gain", "rope_positions", "rope_tables", "apply_rope",
+    "segment_ids", "allowed_mask", "attention", "gelu_tanh", "block_forward",
+    "quantize_block_weights", "dit_step", "euler_update", "rel_l2", "HEAD_DIM",
+    "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
+]
+
+HEAD_DIM = 128
+ROPE_AXES = (32, 48, 48)   # frame, height, width share of the head dim
+ROPE_THETA = 10000.0
+LN_EPS = 1e-6
+QK_EPS = 1e-6
+
+
+# ----------------------------------------------------------------------------- rounding
+
+def round_bf16(a) -> np.ndarray:
+    """Nearest bfloat16 value of each element (ties to even), as float64.
+
+    bf16 keeps 7 of fp64's 52 explicit mantissa bits; the low 45 bits are
+    rounded off on the integer view.  Valid for finite values in the normal
+    bf16 range, which is all the block produces.
+    """
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    bits = a.view(np.uint64)
+    lsb = (bits >> np.uint64(45)) & np.uint64(1)
+    bits = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
+    return bits.view(np.float64)
+
+
+def _store(a, mode: str):
+    return a if mode == "f32" else round_bf16(a)
+
+
+# ----------------------------------------------------------------------------- W8A8
+
+def quantize_rows(a) -> Tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-row int8 quantization with fp32 scales.
+
+    [FlagOS, Quantization and validation]: int8 weights are symmetric per
+    output channel with zero point 0 and fp32 scales; activations are
+    quantized dynamically per token.  Reading: the activation side uses the
+    same symmetric rule (the workloads ask for symmetric activations), with
+    s = amax/127 in fp32, q = clamp(round_half_even(a/s), -127, 127) using an
+    IEEE fp32 division, and an all-zero row giving s = 0 and q = 0.  The values
+    must be exactly representable in fp32 (they are bf16 or fp32 tensors).
+    Returns (q int8 [..., K], s float32 [...]).
+    """
+    a64 = np.asarray(a, dtype=np.float64)
+    a32 = a64.astype(np.float32)
+    if not np.array_equal(a32.astype(np.float64), a64):
+        raise ValueError("quantize_rows: input not representable in fp32")
+    amax = np.max(np.abs(a32), axis=-1)
+    s = (amax / np.float32(127.0)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    r = (a32 / safe[..., None]).astype(np.float32)
+    q = np.clip(np.rint(r), -127, 127)
+    q[s == 0] = 0
+    return q.astype(np.int8), s
+
+
+def int8_matmul_exact(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """acc[m, n] = sum_k qa[m, k] * qw[n, k] exactly, as int64.
+
+    [FlagOS, Quantization and validation]: int32 accumulation.  With codes in
+    [-127, 127] every partial sum is an integer below K*127^2 < 2^53, so fp64
+    BLAS returns it exactly whatever its summation order.
+    """
+    K = qa.shape[-1]
+    assert qw.shape[-1] == K
+    assert K * 127 * 127 < 2 ** 53
+    return np.rint(qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+
+
+def w8a8_linear(qa, sa, qw, sw, bias) -> np.ndarray:
+    """y = acc * s_a[m] * s_w[n] + b[n] in fp64 ([FlagOS]: fp32 scaling after int32 accumulation)."""
+    acc = int8_matmul_exact(qa, qw).astype(np.float64)
+    y = acc * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
+
+
+def linear(a, w, bias) -> np.ndarray:
+    """y = a @ w.T + b in fp64; w is [N, K]."""
+    y = np.asarray(a, np.float64) @ np.asarray(w, np.float64).T
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
+
+
+def quantize_block_weights(weights: Dict[str, np.ndarray]) -> Dict[str, Tuple[np.ndarray, np.ndarray]]:
+    """Per-output-channel int8 codes and fp32 scales of the four linear matrices."""
+    return {k: quantize_rows(weights[k]) for k in ("w_qkv", "w_o", "w_1", "w_2")}
+
+
+# ----------------------------------------------------------------------------- norms
+
+def adaln_modulate(x, shift, scale, eps: float = LN_EPS) -> np.ndarray:
+    """LayerNorm without affine (biased variance) followed by x_hat*(1+scale)+shift.
+
+    [MNN, What runs where] names the per-block modulation rows; the reading is
+    the plain adaLN form with (shift, scale) rows broadcast per token.
+    """
+    x = np.asarray(x, np.float64)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    xhat = (x - mu) / np.sqrt(var + eps)
+    return xhat * (1.0 + np.asarray(scale, np.float64)) + np.asarray(shift, np.float64)
+
+
+def qk_rmsnorm(t, g, mode: str, eps: float = QK_EPS) -> np.ndarray:
+    """Per-head RMSNorm over the 128 head dims, with a learned gain g [128].
+
+    [mere, Numerical checks]: the normalized activation is cast to the gain's
+    dtype (bf16 in the bf16 modes) before it is multiplied by the gain; the
+    product is a bf16 tensor again.
+    """
+    t = np.asarray(t, np.float64)
+    n = t / np.sqrt((t * t).mean(axis=-1, keepdims=True) + eps)
+    return apply_gain(n, g, mode)
+
+
+def apply_gain(n, g, mode: str) -> np.ndarray:
+    """Gain step of the Q/K RMSNorm: in the bf16 modes, round n to bf16, multiply, round again."""
+    if mode == "f32":
+        return np.asarray(n, np.float64) * np.asarray(g, np.float64)
+    return round_bf16(round_bf16(n) * np.asarray(g, np.float64))
+
+
+# ----------------------------------------------------------------------------- RoPE
+
+def rope_positions(text_len: int, grids: Sequence[Tuple[int, int]]) -> np.ndarray:
+    """(frame, height, width) position of every token of [text | image_0 | image_1 ...].
+
+    [CoreAI, Graph contracts]: text token i sits at (i, i, i); image token (y, x)
+    of an h x w grid, in raster order, sits at (L, y - (h - h//2), x - (w - w//2))
+    with L the text length.  Reading for a second image segment: the k-th image
+    segment (0-based) takes frame L + k.
+    """
+    pos = [(i, i, i) for i in range(text_len)]
+    for k, (h, w) in enumerate(grids):
+        for y in range(h):
+            for x in range(w):
+                pos.append((text_len + k, y - (h - h // 2), x - (w - w // 2)))
+    return np.array(pos, dtype=np.int64).reshape(-1, 3)
+
+
+def rope_tables(pos: np.ndarray, theta: float = ROPE_THETA, axes=ROPE_AXES):
+    """cos/sin [T, 64], one angle per interleaved pair of head dims.
+
+    [CoreAI, Graph contracts] passes per-token cos/sin of width 64 per stream;
+    [MNN, What runs where] names the 3-axis RoPE.  Axis a owns axes[a] head dims,
+    i.e. axes[a]/2 pairs; pair j of axis a rotates by pos_a * theta^(-2j/axes[a]).
+    Pairs are ordered frame, height, width.
+    """
+    angles = []
+    for a, dim in enumerate(axes):
+        j = np.arange(dim // 2, dtype=np.float64)
+        omega = theta ** (-2.0 * j / dim)
+        angles.append(pos[:, a:a + 1].astype(np.float64) * omega[None, :])
+    phi = np.concatenate(angles, axis=1)
+    return np.cos(phi), np.sin(phi)
+
+
+def apply_rope(t, cos, sin) -> np.ndarray:
+    """Rotate interleaved pairs (t[2m], t[2m+1]) of each head by the token's angle m."""
+    t = np.asarray(t, np.float64)
+    c = np.asarray(cos, np.float64)[:, None, :]
+    s = np.asarray(sin, np.float64)[:, None, :]
+    ev, od = t[..., 0::2], t[..., 1::2]
+    out = np.empty_like(t)
+    out[..., 0::2] = ev * c - od * s
+    out[..., 1::2] = ev * s + od * c
+    return out
+
+
+# ----------------------------------------------------------------------------- attention
+
+def segment_ids(seg_len: Sequence[int]) -> np.ndarray:
+    return np.repeat(np.arange(len(seg_len)), np.asarray(seg_len, dtype=np.int64))
+
+
+def allowed_mask(seg_len: Sequence[int], T_q: int) -> np.ndarray:
+    """allowed[i, j]: query row i (absolute position T_k - T_q + i) may attend key j.
+
+    [CoreAI, intro] and [MNN, What runs where]: the single-stream DiT attends
+    block-causally over its segments.  Reading: every segment sees itself
+    bidirectionally and all earlier segments.
+    """
+    seg = segment_ids(seg_len)
+    T_k = seg.shape[0]
+    sq = seg[T_k - T_q:]
+    return seg[None, :] <= sq[:, None]
+
+
+def attention(q, k, v, seg_len: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
+    """Block-causal softmax attention per head, fp64.
+
+    q [T_q, H, d], k and v [T_k, H, d]; query row i is at absolute position
+    T_k - T_q + i, so a prefix of keys may come from a cache.
+    """
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    T_q, H, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    allowed = allowed_mask(seg_len, T_q)
+    out = np.empty_like(q)
+    for h in range(H):
+        s = (q[:, h, :] @ k[:, h, :].T) * scale
+        s = np.where(allowed, s, -np.inf)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, h, :]
+    return out
+
+
+# ----------------------------------------------------------------------------- MLP
+
+def gelu_tanh(u) -> np.ndarray:
+    """tanh-approximated GELU (the workloads' MLP activation)."""
+    u = np.asarray(u, np.float64)
+    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+
+
+# ----------------------------------------------------------------------------- block
+
+def _row_mod(mod, mod_of_seg, seg_len, T_q) -> np.ndarray:
+    """[T_q, 6, D] modulation rows of each computed token (by its segment's set)."""
+    seg = segment_ids(seg_len)
+    rows_seg = seg[seg.shape[0] - T_q:]
+    return np.asarray(mod, np.float64)[np.asarray(mod_of_seg)[rows_seg]]
+
+
+def _lin(a, name, weights, qweights, mode):
+    if mode == "w8a8":
+        qa, sa = quantize_rows(a)
+        qw, sw = qweights[name]
+        return w8a8_linear(qa, sa, qw, sw, weights["b" + name[1:]])
+    return linear(a, weights[name], weights["b" + name[1:]])
+
+
+def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
+                  k_prefix=None, v_prefix=None, qweights=None,
+                  ln_eps: float = LN_EPS, qk_eps: float = QK_EPS) -> Dict[str, np.ndarray]:
+    """Forward of one single-stream DiT block on the last T_q rows of the sequence.
+
+    x [T_q, D]: the rows computed by this call (the whole sequence, or the target
+    rows when the prefix K/V come from a cache).  mod [n_sets, 6, D] holds rows
+    (shift1, scale1, gate1, shift2, scale2, gate2); mod_of_seg maps each segment
+    to its set.  cos/sin [T_q, 64] belong to the computed rows.  k_prefix/v_prefix
+    [T_k - T_q, H, 128] are the cached K/V of the earlier rows (post-norm,
+    post-RoPE K and plain V).
+
+    Order (reading: pre-norm adaLN with gated residuals, the arrangement that uses
+    six modulation rows and a gated residual):
+      h  = LN(x)(1+scale1)+shift1;  [q|k|v] = h Wqkv^T + b
+      q, k <- RoPE(RMSNorm_head(q, k) * g)   (cast before gain [mere])
+      o  = block-causal attention(q, [k_prefix; k], [v_prefix; v])
+      x1 = x + gate1 * (o Wo^T + bo)
+      h2 = LN(x1)(1+scale2)+shift2
+      x2 = x1 + gate2 * (GELU_tanh(h2 W1^T + b1) W2^T + b2)
+    Returns x_out and the new K/V rows plus intermediates.
+    """
+    x = np.asarray(x, np.float64)
+    T_q, D = x.shape
+    H = D // HEAD_DIM
+    if mode == "w8a8" and qweights is None:
+        qweights = quantize_block_weights(weights)
+    m = _row_mod(mod, mod_of_seg, seg_len, T_q)
+    shift1, scale1, gate1, shift2, scale2, gate2 = (m[:, i, :] for i in range(6))
+
+    h = _store(adaln_modulate(x, shift1, scale1, ln_eps), mode)
+    qkv = _store(_lin(h, "w_qkv", weights, qweights, mode), mode)
+    q = qkv[:, :D].reshape(T_q, H, HEAD_DIM)
+    k = qkv[:, D:2 * D].reshape(T_q, H, HEAD_DIM)
+    v = qkv[:, 2 * D:].reshape(T_q, H, HEAD_DIM)
+    q = _store(apply_rope(qk_rmsnorm(q, weights["g_q"], mode, qk_eps), cos, sin), mode)
+    k = _store(apply_rope(qk_rmsnorm(k, weights["g_k"], mode, qk_eps), cos, sin), mode)
+    if k_prefix is not None and len(k_prefix):
+        k_all = np.concatenate([np.asarray(k_prefix, np.float64), k], axis=0)
+        v_all = np.concatenate([np.asarray(v_prefix, np.float64), v], axis=0)
+    else:
+        k_all, v_all = k, v
+    o = _store(attention(q, k_all, v_all, seg_len), mode).reshape(T_q, D)
+    y = _store(_lin(o, "w_o", weights, qweights, mode), mode)
+    x1 = _store(x + gate1 * y, mode)
+    h2 = _store(adaln_modulate(x1, shift2, scale2, ln_eps), mode)
+    u = _store(_lin(h2, "w_1", weights, qweights, mode), mode)
+    g = _store(gelu_tanh(u), mode)
+    y2 = _store(_lin(g, "w_2", weights, qweights, mode), mode)
+    x2 = _store(x1 + gate2 * y2, mode)
+    return {"x_out": x2, "k": k, "v": v, "q": q, "h": h, "qkv": qkv, "o": o,
+            "x1": x1, "h2": h2, "u": u, "g": g}
+
+
+# ----------------------------------------------------------------------------- one denoise step
+
+def euler_update(latent, v, sigma: float, sigma_next: float) -> np.ndarray:
+    """FlowMatch Euler step x + (sigma_next - sigma) * v  ([CoreAI, Graph contracts])."""
+    return np.asarray(latent, np.float64) + (float(sigma_next) - float(sigma)) * np.asarray(v, np.float64)
+
+
+def dit_step(step_in: Dict[str, np.ndarray], blocks, mod, mod_of_seg, seg_len, cos, sin, mode: str):
+    """One denoise step: DiT head, the block stack, DiT tail, Euler update.
+
+    [CoreAI, Graph contracts]: the DiT takes the packed latent [N, 64] and text
+    features [L, D] and returns a velocity [N, 64]; the sampler then makes one
+    Euler update.  Reading for the head and tail, which the pages do not spell
+    out: img_in = Linear(64 -> D), txt_in = Linear(D -> D); tail = LN with a
+    (shift, scale) modulation pair, then proj_out = Linear(D -> 64) on the image
+    rows.  ``blocks`` yields (weights, qweights-or-None) per block.
+    """
+    lat = np.asarray(step_in["latent"], np.float64)
+    x_img = _store(linear(_store(lat, mode), step_in["w_img_in"], step_in["b_img_in"]), mode)
+    x_txt = _store(linear(step_in["txt_feats"], step_in["w_txt_in"], step_in["b_txt_in"]), mode)
+    x = np.concatenate([x_txt, x_img], axis=0)
+    for weights, qweights in blocks:
+        x = block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode, qweights=qweights)["x_out"]
+    L = x_txt.shape[0]
+    mf = np.asarray(step_in["mod_final"], np.float64)[0]
+    hf = _store(adaln_modulate(x[L:], mf[0], mf[1]), mode)
+    vel = _store(linear(hf, step_in["w_proj_out"], step_in["b_proj_out"]), mode)
+    return {"latent_next": euler_update(lat, vel, step_in["sigma"], step_in["sigma_next"]),
+            "vel": vel, "x_blocks": x}
+
+
+def rel_l2(y, y_ref) -> float:
+    """||y - y_ref||_2 / ||y_ref||_2 over the whole tensor, in fp64."""
+    y = np.asarray(y, np.float64)
+    y_ref = np.asarray(y_ref, np.float64)
+    return float(np.linalg.norm((y - y_ref).ravel()) / np.linalg.norm(y_ref.ravel()))

@@ -1,0 +1,193 @@
+"""Pins of the oracle's whole block and denoise step (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+import ditsynth
+import oracle
+
+
+def _tiny(mode="f32", seed=7, grids=((2, 2),), text=3, D=256, F=512):
+    w = ditsynth.custom("tiny", D, D // 128, F, text, grids, mode, seed)
+    return w, ditsynth.block_weights(w), ditsynth.block_inputs(w)
+
+
+def _brute_block(w, wt, inp):
+    """The block with explicit loops over tokens, heads and pairs (fp64)."""
+    x = inp["x"].astype(np.float64)
+    wt = {k: np.asarray(v, np.float64) for k, v in wt.items()}   # no fp32 scalar arithmetic
+    T, D = x.shape
+    H = D // 128
+    mod = inp["mod"][0].astype(np.float64)
+    # positions, worked token by token
+    pos = [(i, i, i) for i in range(w.text)]
+    for kk, (gh, gw) in enumerate(w.images):
+        for y in range(gh):
+            for xx in range(gw):
+                pos.append((w.text + kk, y - (gh - gh // 2), xx - (gw - gw // 2)))
+    seg = []
+    for s, n in enumerate(w.seg_len):
+        seg += [s] * n
+
+    def ln_mod(rowv, shift, scale):
+        mu = sum(rowv) / D
+        var = sum((a - mu) ** 2 for a in rowv) / D
+        return [((rowv[c] - mu) / math.sqrt(var + 1e-6)) * (1 + scale[c]) + shift[c] for c in range(D)]
+
+    def lin(vec, W, b):
+        return [float(np.dot(W[n], vec)) + b[n] for n in range(W.shape[0])]
+
+    def angle(p, m):
+        axes = (32, 48, 48)
+        start = 0
+        for a, dim in enumerate(axes):
+            if m < start + dim // 2:
+                j = m - start
+                return p[a] * 10000.0 ** (-2.0 * j / dim)
+            start += dim // 2
+        raise AssertionError
+
+    qs, ks, vs = [], [], []
+    for t in range(T):
+        h = ln_mod(list(x[t]), mod[0], mod[1])
+        qkv = lin(np.array(h), wt["w_qkv"], wt["b_qkv"])
+        qh, kh, vh = [], [], []
+        for head in range(H):
+            for part, gain, dst in ((0, wt["g_q"], qh), (1, wt["g_k"], kh)):
+                vec = qkv[part * D + head * 128: part * D + head * 128 + 128]
+                rms = math.sqrt(sum(a * a for a in vec) / 128 + 1e-6)
+                nv = [vec[c] / rms * gain[c] for c in range(128)]
+                rv = [0.0] * 128
+                for m in range(64):
+                    phi = angle(pos[t], m)
+                    rv[2 * m] = nv[2 * m] * math.cos(phi) - nv[2 * m + 1] * math.sin(phi)
+                    rv[2 * m + 1] = nv[2 * m] * math.sin(phi) + nv[2 * m + 1] * math.cos(phi)
+                dst.append(rv)
+            vh.append(qkv[2 * D + head * 128: 2 * D + head * 128 + 128])
+        qs.append(qh)
+        ks.append(kh)
+        vs.append(vh)
+    out = np.zeros_like(x)
+    for t in range(T):
+        o = []
+        for head in range(H):
+            sc = [(j, np.dot(qs[t][head], ks[j][head]) / math.sqrt(128)) for j in range(T) if seg[j] <= seg[t]]
+            mx = max(s for _, s in sc)
+            z = sum(math.exp(s - mx) for _, s in sc)
+            acc = np.zeros(128)
+            for j, s in sc:
+                acc += math.exp(s - mx) / z * np.array(vs[j][head])
+            o += list(acc)
+        y = lin(np.array(o), wt["w_o"], wt["b_o"])
+        x1 = [x[t, c] + mod[2][c] * y[c] for c in range(D)]
+        h2 = ln_mod(x1, mod[3], mod[4])
+        u = lin(np.array(h2), wt["w_1"], wt["b_1"])
+        g = [0.5 * a * (1 + math.tanh(math.sqrt(2 / math.pi) * (a + 0.044715 * a ** 3))) for a in u]
+        y2 = lin(np.array(g), wt["w_2"], wt["b_2"])
+        out[t] = [x1[c] + mod[5][c] * y2[c] for c in range(D)]
+    return out
+
+
+def _run(w, wt, inp, mode=None, **kw):
+    pos = oracle.rope_positions(w.text, w.images)
+    c, s = oracle.rope_tables(pos)
+    T_q = inp["x"].shape[0]
+    return oracle.block_forward(inp["x"], inp["mod"], inp["mod_of_seg"], inp["seg_len"],
+                                c[-T_q:], s[-T_q:], wt, mode or w.mode, **kw)
+
+
+def test_block_matches_brute_force_loops():
+    w, wt, inp = _tiny()
+    got = _run(w, wt, inp)["x_out"]
+    ref = _brute_block(w, wt, inp)
+    assert np.allclose(got, ref, rtol=1e-11, atol=1e-11)
+
+
+def test_zero_gates_give_identity_in_every_mode():
+    for mode in ("f32", "bf16", "w8a8"):
+        w, wt, inp = _tiny(mode)
+        inp["mod"][:, 2, :] = 0.0
+        inp["mod"][:, 5, :] = 0.0
+        out = _run(w, wt, inp)["x_out"]
+        assert np.array_equal(out, inp["x"].astype(np.float64)), mode
+
+
+def test_later_segments_do_not_change_earlier_rows():
+    for mode in ("f32", "w8a8"):
+        w, wt, inp = _tiny(mode, grids=((2, 2), (2, 3)))
+        o1 = _run(w, wt, inp)["x_out"]
+        inp2 = dict(inp)
+        x2 = inp["x"].copy()
+        x2[7:] = x2[7:] * 2 + 1
+        inp2["x"] = ditsynth.to_bf16_grid(x2) if mode != "f32" else x2
+        o2 = _run(w, wt, inp2)["x_out"]
+        assert np.array_equal(o1[:7], o2[:7]), mode
+        assert not np.allclose(o1[7:], o2[7:])
+
+
+def test_prefix_cache_equals_uncached():
+    for mode in ("f32", "bf16", "w8a8"):
+        w = ditsynth.custom("pc", 256, 2, 512, 3, [(2, 2), (3, 3)], mode, 12, steps=2)
+        wt = ditsynth.block_weights(w)
+        qw = oracle.quantize_block_weights(wt) if mode == "w8a8" else None
+        pos = oracle.rope_positions(w.text, w.images)
+        c, s = oracle.rope_tables(pos)
+        # step 1 uncached: writes the prefix K/V
+        i1 = ditsynth.block_inputs(w, step=0)
+        r1 = oracle.block_forward(i1["x"], i1["mod"], i1["mod_of_seg"], i1["seg_len"], c, s, wt, mode, qweights=qw)
+        P = w.prefix_len
+        # step 2 uncached vs cached
+        i2 = ditsynth.block_inputs(w, step=1)
+        assert np.array_equal(i1["x"][:P], i2["x"][:P])
+        full = oracle.block_forward(i2["x"], i2["mod"], i2["mod_of_seg"], i2["seg_len"], c, s, wt, mode, qweights=qw)
+        cached = oracle.block_forward(i2["x"][P:], i2["mod"], i2["mod_of_seg"], i2["seg_len"], c[P:], s[P:], wt, mode,
+                                      k_prefix=r1["k"][:P], v_prefix=r1["v"][:P], qweights=qw)
+        assert np.allclose(cached["x_out"], full["x_out"][P:], rtol=1e-12, atol=1e-12), mode
+        assert not np.allclose(full["x_out"][P:], r1["x_out"][P:])
+
+
+def test_w8a8_is_close_to_bf16_with_dequantized_weights():
+    w, wt, inp = _tiny("w8a8", D=512, F=2048, grids=((4, 4),), text=8)
+    qw = oracle.quantize_block_weights(wt)
+    deq = dict(wt)
+    for k, (q, s) in qw.items():
+        deq[k] = q.astype(np.float64) * s[:, None].astype(np.float64)
+    a = _run(w, wt, inp, "w8a8", qweights=qw)["x_out"]
+    b = _run(w, deq, inp, "bf16")["x_out"]
+    x = inp["x"].astype(np.float64)
+    e = oracle.rel_l2(a - x, b - x)
+    assert 1e-4 < e < 3e-2
+
+
+def test_bf16_mode_stays_within_bf16_noise_of_fp64():
+    w, wt, inp = _tiny("bf16", D=512, F=2048, grids=((4, 4),), text=8)
+    a = _run(w, wt, inp, "bf16")["x_out"]
+    b = _run(w, wt, inp, "f32")["x_out"]
+    x = inp["x"].astype(np.float64)
+    assert oracle.rel_l2(a, b) < 2 ** -8
+    assert oracle.rel_l2(a - x, b - x) < 0.05
+
+
+def test_euler_closed_form():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((4, 64))
+    v = rng.standard_normal((4, 64))
+    assert np.array_equal(oracle.euler_update(x, v, 0.7, 0.7), x)
+    assert np.allclose(oracle.euler_update(x, v, 1.0, 0.5), x - 0.5 * v, atol=0)
+
+
+def test_dit_step_shapes_and_zero_velocity_identity():
+    w = ditsynth.custom("st", 256, 2, 512, 4, [(2, 2)], "bf16", 3, n_blocks=2)
+    st = ditsynth.step_inputs(w)
+    inp = ditsynth.block_inputs(w)
+    pos = oracle.rope_positions(w.text, w.images)
+    c, s = oracle.rope_tables(pos)
+    blocks = [(ditsynth.block_weights(w, b), None) for b in range(2)]
+    r = oracle.dit_step(st, blocks, inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, "bf16")
+    assert r["latent_next"].shape == (4, 64) and r["vel"].shape == (4, 64)
+    st0 = dict(st)
+    st0["w_proj_out"] = np.zeros_like(st["w_proj_out"])
+    st0["b_proj_out"] = np.zeros_like(st["b_proj_out"])
+    r0 = oracle.dit_step(st0, blocks, inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, "bf16")
+    assert np.array_equal(r0["latent_next"], st["latent"].astype(np.float64))
