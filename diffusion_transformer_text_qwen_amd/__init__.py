@@ -1,0 +1,277 @@
+"""Python binding of the gfx950 single-stream DiT block library (libditblock.so).
+
+Argument marshalling only: every function passes torch tensor addresses and
+the current HIP stream to the C ABI declared in ``include/dit.h``; all
+arithmetic runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libditblock.so")
+
+F32, BF16, I8, I32 = 0, 1, 2, 3
+MODE_F32, MODE_BF16, MODE_W8A8 = 0, 1, 2
+MODES = {"f32": MODE_F32, "bf16": MODE_BF16, "w8a8": MODE_W8A8}
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_fp = ctypes.c_float
+
+
+class DitError(RuntimeError):
+    def __init__(self, status: int, name: str, detail: str):
+        super().__init__(f"{name} failed with status {status}: {detail}")
+        self.status = status
+
+
+class BlockConfig(ctypes.Structure):
+    _fields_ = [("mode", _c_i32), ("D", _c_i32), ("H", _c_i32), ("head_dim", _c_i32), ("F", _c_i32),
+                ("ln_eps", _fp), ("qk_eps", _fp)]
+
+
+class BlockWeightsC(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("w_qkv", "w_o", "w_1", "w_2", "s_qkv", "s_o", "s_1", "s_2",
+                                   "b_qkv", "b_o", "b_1", "b_2", "g_q", "g_k")]
+
+
+class BlockIO(ctypes.Structure):
+    _fields_ = [("x", _vp), ("mod", _vp), ("n_mod", _c_i32), ("mod_of_seg", _vp), ("cos_t", _vp),
+                ("sin_t", _vp), ("seg_len", _vp), ("n_seg", _c_i32), ("T_q", _c_i64), ("T_k", _c_i64),
+                ("k_cache", _vp), ("v_cache", _vp)]
+
+
+_SIGS = {
+    "dit_abi_version": ([], ctypes.c_int),
+    "dit_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "dit_last_error": ([], ctypes.c_char_p),
+    "dit_quantize_rows": ([_vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp], ctypes.c_int),
+    "w8a8_linear": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp, _vp],
+                    ctypes.c_int),
+    "bf16_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp],
+                    ctypes.c_int),
+    "f32_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _c_i64, _vp], ctypes.c_int),
+    "block_causal_attention": ([_vp, _vp, _vp, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64,
+                                _c_i64, _c_i64, _c_i64, _vp, _c_i32, _fp, _vp], ctypes.c_int),
+    "dit_rope_tables": ([_c_i32, _vp, _c_i32, _c_i64, _c_i64, _fp, _vp, _vp, _vp], ctypes.c_int),
+    "dit_qk_norm_rope": ([_vp, ctypes.c_int, _c_i64, _c_i32, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _c_i64, _vp,
+                          _c_i64, _vp], ctypes.c_int),
+    "dit_adaln_modulate": ([_vp, ctypes.c_int, _c_i64, _c_i64, _vp, _vp, _fp, _vp, ctypes.c_int, _vp, _vp,
+                            _vp], ctypes.c_int),
+    "dit_euler_step": ([_vp, _vp, ctypes.c_int, _c_i64, _fp, _fp, _vp], ctypes.c_int),
+    "dit_cast": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _c_i64, _vp], ctypes.c_int),
+    "dit_block_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64], ctypes.c_size_t),
+    "dit_block_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), ctypes.POINTER(BlockIO),
+                           _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "dit_stack_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), _c_i32,
+                           ctypes.POINTER(BlockIO), _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libditblock.so (built by ``build.py``); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run diffusion_transformer_text_qwen_amd/build.py")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(l, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = l
+    return _lib
+
+
+def exported_symbols() -> List[str]:
+    return list(_SIGS)
+
+
+def _check(status: int, name: str) -> None:
+    if status != 0:
+        raise DitError(status, name, lib().dit_last_error().decode())
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    return {torch.float32: F32, torch.bfloat16: BF16, torch.int8: I8, torch.int32: I32}[t.dtype]
+
+
+def _host_i32(seq) -> ctypes.Array:
+    arr = (ctypes.c_int32 * len(seq))(*[int(v) for v in seq])
+    return arr
+
+
+# ---------------------------------------------------------------- op-level calls
+
+def quantize_rows(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=None) -> None:
+    M, K = x.shape
+    _check(lib().dit_quantize_rows(_p(x), _dt(x), M, K, x.stride(0), _p(q), _p(scale), _stream(stream)),
+           "dit_quantize_rows")
+
+
+def w8a8_linear(a, a_scale, w, w_scale, bias, y, acc_out=None, stream=None) -> None:
+    M, K = a.shape
+    N = w.shape[0]
+    _check(lib().w8a8_linear(_p(a), _p(a_scale), M, K, _p(w), _p(w_scale), _p(bias), N, _p(y), _dt(y),
+                             y.stride(0), _p(acc_out), _stream(stream)), "w8a8_linear")
+
+
+def bf16_linear(a, w, bias, y, stream=None) -> None:
+    M, K = a.shape
+    N = w.shape[0]
+    _check(lib().bf16_linear(_p(a), M, K, a.stride(0), _p(w), _p(bias), N, _p(y), _dt(y), y.stride(0),
+                             _stream(stream)), "bf16_linear")
+
+
+def f32_linear(a, w, bias, y, stream=None) -> None:
+    M, K = a.shape
+    N = w.shape[0]
+    _check(lib().f32_linear(_p(a), M, K, a.stride(0), _p(w), _p(bias), N, _p(y), y.stride(0),
+                            _stream(stream)), "f32_linear")
+
+
+def block_causal_attention(q, k, v, o, seg_len: Sequence[int], sm_scale: float = 0.0, stream=None) -> None:
+    """q [T_q, H, 128], k/v [T_k, H, 128], o [T_q, H, 128] (row-contiguous per token)."""
+    T_q, H, d = q.shape
+    T_k = k.shape[0]
+    segs = _host_i32(seg_len)
+    _check(lib().block_causal_attention(_p(q), _p(k), _p(v), _p(o), _dt(q), T_q, T_k, H, d, q.stride(0),
+                                        k.stride(0), v.stride(0), o.stride(0), ctypes.cast(segs, _vp),
+                                        len(seg_len), sm_scale, _stream(stream)), "block_causal_attention")
+
+
+def rope_tables(text_len: int, grids, row0: int, T_rows: int, cos_out, sin_out, theta: float = 10000.0,
+                stream=None) -> None:
+    flat = [int(v) for g in grids for v in g]
+    arr = _host_i32(flat) if flat else None
+    _check(lib().dit_rope_tables(text_len, ctypes.cast(arr, _vp) if arr is not None else None, len(grids),
+                                 row0, T_rows, theta, _p(cos_out), _p(sin_out), _stream(stream)),
+           "dit_rope_tables")
+
+
+def qk_norm_rope(qkv, g_q, g_k, cos_t, sin_t, q_out, k_out, v_out, eps: float = 1e-6, stream=None) -> None:
+    T = qkv.shape[0]
+    H = qkv.shape[1] // (3 * 128)
+    _check(lib().dit_qk_norm_rope(_p(qkv), _dt(qkv), T, H, _p(g_q), _p(g_k), _p(cos_t), _p(sin_t), eps,
+                                  _p(q_out), _p(k_out), k_out.stride(0), _p(v_out), v_out.stride(0),
+                                  _stream(stream)), "dit_qk_norm_rope")
+
+
+def adaln_modulate(x, shift, scale, h_out=None, q_out=None, q_scale=None, eps: float = 1e-6,
+                   stream=None) -> None:
+    M, D = x.shape
+    hdt = _dt(h_out) if h_out is not None else _dt(x)
+    _check(lib().dit_adaln_modulate(_p(x), _dt(x), M, D, _p(shift), _p(scale), eps, _p(h_out), hdt,
+                                    _p(q_out), _p(q_scale), _stream(stream)), "dit_adaln_modulate")
+
+
+def euler_step(x, v, sigma: float, sigma_next: float, stream=None) -> None:
+    _check(lib().dit_euler_step(_p(x), _p(v), _dt(v), x.numel(), sigma, sigma_next, _stream(stream)),
+           "dit_euler_step")
+
+
+def cast(x, y, stream=None) -> None:
+    _check(lib().dit_cast(_p(x), _dt(x), _p(y), _dt(y), x.numel(), _stream(stream)), "dit_cast")
+
+
+# ---------------------------------------------------------------- the block
+
+def block_config(mode: str, D: int, H: int, F: int, ln_eps: float = 1e-6, qk_eps: float = 1e-6) -> BlockConfig:
+    return BlockConfig(MODES[mode], D, H, 128, F, ln_eps, qk_eps)
+
+
+class BlockWeights:
+    """Device-resident weights of one block in the layout the library reads.
+
+    From fp32 host arrays ``w_*`` ([N, K]), ``b_*``, ``g_q``, ``g_k``: in W8A8
+    mode the matrices are uploaded as fp32 masters and quantized per output
+    channel on the GPU (``dit_quantize_rows``), then the masters are freed.
+    """
+
+    def __init__(self, arrays: Dict, mode: str, device="cuda"):
+        self.mode = mode
+        self.t: Dict[str, torch.Tensor] = {}
+        for name in ("w_qkv", "w_o", "w_1", "w_2"):
+            a = torch.as_tensor(arrays[name])
+            if mode == "w8a8":
+                master = a.to(device=device, dtype=torch.float32).contiguous()
+                q = torch.empty(master.shape, dtype=torch.int8, device=device)
+                s = torch.empty(master.shape[0], dtype=torch.float32, device=device)
+                quantize_rows(master, q, s)
+                self.t[name] = q
+                self.t["s" + name[1:]] = s
+                del master
+            elif mode == "bf16":
+                self.t[name] = a.to(device=device, dtype=torch.float32).to(torch.bfloat16).contiguous()
+            else:
+                self.t[name] = a.to(device=device, dtype=torch.float32).contiguous()
+        for name in ("b_qkv", "b_o", "b_1", "b_2", "g_q", "g_k"):
+            self.t[name] = torch.as_tensor(arrays[name]).to(device=device, dtype=torch.float32).contiguous()
+        self.c = BlockWeightsC(**{n: (self.t[n].data_ptr() if n in self.t else None)
+                                  for n, _ in BlockWeightsC._fields_})
+
+    @classmethod
+    def from_device(cls, tensors: Dict[str, torch.Tensor], mode: str) -> "BlockWeights":
+        obj = cls.__new__(cls)
+        obj.mode = mode
+        obj.t = dict(tensors)
+        obj.c = BlockWeightsC(**{n: (obj.t[n].data_ptr() if n in obj.t else None) for n, _ in BlockWeightsC._fields_})
+        return obj
+
+
+def workspace_bytes(cfg: BlockConfig, T_q: int, T_k: int) -> int:
+    return int(lib().dit_block_workspace_bytes(ctypes.byref(cfg), T_q, T_k))
+
+
+def _io(x, mod, mod_of_seg, cos_t, sin_t, seg_len, T_k, k_cache, v_cache):
+    mos = _host_i32(mod_of_seg)
+    segs = _host_i32(seg_len)
+    io = BlockIO(x=_p(x), mod=_p(mod), n_mod=mod.shape[0], mod_of_seg=ctypes.cast(mos, _vp), cos_t=_p(cos_t),
+                 sin_t=_p(sin_t), seg_len=ctypes.cast(segs, _vp), n_seg=len(seg_len), T_q=x.shape[0], T_k=T_k,
+                 k_cache=_p(k_cache), v_cache=_p(v_cache))
+    return io, (mos, segs)
+
+
+def block_forward(cfg: BlockConfig, w: BlockWeights, x, mod, mod_of_seg, cos_t, sin_t, seg_len, k_cache, v_cache,
+                  workspace, stream=None) -> None:
+    """x [T_q, D] updated in place; k_cache/v_cache [T_k, H, 128]."""
+    T_k = int(sum(seg_len))
+    io, keep = _io(x, mod, mod_of_seg, cos_t, sin_t, seg_len, T_k, k_cache, v_cache)
+    _check(lib().dit_block_forward(ctypes.byref(cfg), ctypes.byref(w.c), ctypes.byref(io), _p(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dit_block_forward")
+    del keep
+
+
+def stack_forward(cfg: BlockConfig, ws: Sequence[BlockWeights], x, mod, mod_of_seg, cos_t, sin_t, seg_len,
+                  k_caches, v_caches, workspace, stream=None) -> None:
+    T_k = int(sum(seg_len))
+    n = len(ws)
+    arr = (BlockWeightsC * n)(*[w.c for w in ws])
+    kc = (_vp * n)(*[_p(t) for t in k_caches])
+    vc = (_vp * n)(*[_p(t) for t in v_caches])
+    io, keep = _io(x, mod, mod_of_seg, cos_t, sin_t, seg_len, T_k, None, None)
+    _check(lib().dit_stack_forward(ctypes.byref(cfg), arr, n, ctypes.byref(io), ctypes.cast(kc, _vp),
+                                   ctypes.cast(vc, _vp), _p(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dit_stack_forward")
+    del keep

@@ -1,0 +1,528 @@
+// C ABI of the block library: argument checks (before any HIP call), the
+// block's workspace plan and the launch sequence of one block.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/dit.h"
+#include "kernels.h"
+
+using namespace dit;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return DIT_OK;
+    return fail(DIT_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define CHECK(cond, code, ...)                  \
+    do {                                        \
+        if (!(cond)) return fail(code, __VA_ARGS__); \
+    } while (0)
+
+#define RUN(expr, what)                          \
+    do {                                         \
+        int _s = hip_status((expr), what);       \
+        if (_s != DIT_OK) return _s;             \
+    } while (0)
+
+hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+constexpr int64_t kMaxK8 = 133144;   // K * 127^2 < 2^31
+
+int check_segs(const int32_t* seg_len, int32_t n_seg, int64_t T_k) {
+    CHECK(seg_len != nullptr, DIT_E_NULL, "seg_len is NULL");
+    CHECK(n_seg >= 1 && n_seg <= kMaxSeg, DIT_E_UNSUPPORTED, "n_seg=%d outside [1, %d]", n_seg, kMaxSeg);
+    int64_t sum = 0;
+    for (int i = 0; i < n_seg; ++i) {
+        CHECK(seg_len[i] >= 0, DIT_E_SHAPE, "seg_len[%d]=%d < 0", i, seg_len[i]);
+        sum += seg_len[i];
+    }
+    CHECK(sum == T_k, DIT_E_SHAPE, "sum(seg_len)=%lld != T_k=%lld", (long long)sum, (long long)T_k);
+    return DIT_OK;
+}
+
+AttnSegs make_attn_segs(const int32_t* seg_len, int32_t n_seg) {
+    AttnSegs a{};
+    int64_t acc = 0;
+    for (int i = 0; i < n_seg; ++i) {
+        acc += seg_len[i];
+        a.end[i] = acc;
+    }
+    a.n = n_seg;
+    return a;
+}
+
+SegMap make_segmap(const int32_t* seg_len, const int32_t* mod_of_seg, int32_t n_seg, int64_t row_offset) {
+    SegMap m{};
+    int64_t acc = 0;
+    for (int i = 0; i < n_seg; ++i) {
+        acc += seg_len[i];
+        m.end[i] = acc;
+        m.set[i] = mod_of_seg ? mod_of_seg[i] : 0;
+    }
+    m.n = n_seg;
+    m.row_offset = row_offset;
+    return m;
+}
+
+EpiParams store_epi(void* y, int64_t ldy, bool y_bf16, const float* bias) {
+    EpiParams ep{};
+    ep.kind = EPI_STORE;
+    ep.act_bf16 = y_bf16;
+    ep.y_bf16 = y_bf16;
+    ep.bias = bias;
+    ep.y = y;
+    ep.ldy = ldy;
+    return ep;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dit_abi_version(void) { return DIT_ABI_VERSION; }
+
+const char* dit_status_string(int s) {
+    switch (s) {
+        case DIT_OK: return "ok";
+        case DIT_E_NULL: return "null pointer";
+        case DIT_E_SHAPE: return "bad shape";
+        case DIT_E_DTYPE: return "bad dtype or mode";
+        case DIT_E_ALIGN: return "misaligned pointer or stride";
+        case DIT_E_UNSUPPORTED: return "unsupported size";
+        case DIT_E_WORKSPACE: return "workspace missing or too small";
+        case DIT_E_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+const char* dit_last_error(void) { return g_err; }
+
+int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                      float* scale, void* stream) {
+    CHECK(x_dtype == DIT_BF16 || x_dtype == DIT_F32, DIT_E_DTYPE, "x_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && ldx >= K, DIT_E_SHAPE, "need M>=0, K>=1, ldx>=K");
+    CHECK(K % 8 == 0 && ldx % 8 == 0, DIT_E_UNSUPPORTED, "K and ldx must be multiples of 8");
+    CHECK(K <= (x_dtype == DIT_BF16 ? 32768 : 16384), DIT_E_UNSUPPORTED, "K=%lld too large", (long long)K);
+    CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
+    if (M == 0) return DIT_OK;
+    CHECK(x && q && scale, DIT_E_NULL, "x, q and scale must be non-NULL");
+    CHECK(aligned16(x) && aligned16(q), DIT_E_ALIGN, "x and q must be 16-byte aligned");
+    RUN(launch_quantize_rows(x, x_dtype == DIT_BF16, M, K, ldx, q, scale, S(stream)), "quantize_rows");
+    return DIT_OK;
+}
+
+int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
+                const float* w_scale, const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy,
+                int32_t* acc_out, void* stream) {
+    CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && N >= 1 && ldy >= N, DIT_E_SHAPE, "need M>=0, K>=1, N>=1, ldy>=N");
+    CHECK(K % 128 == 0, DIT_E_UNSUPPORTED, "K=%lld must be a multiple of 128", (long long)K);
+    CHECK(N % 16 == 0, DIT_E_UNSUPPORTED, "N=%lld must be a multiple of 16", (long long)N);
+    CHECK(K <= kMaxK8, DIT_E_UNSUPPORTED, "K=%lld beyond the int32-safe bound", (long long)K);
+    CHECK(((M + 127) / 128) * ((N + 127) / 128) < 0x7fffffff, DIT_E_UNSUPPORTED, "too many tiles");
+    if (M == 0) return DIT_OK;
+    CHECK(a && a_scale && w && w_scale && y, DIT_E_NULL, "a, a_scale, w, w_scale and y must be non-NULL");
+    CHECK(aligned16(a) && aligned16(w), DIT_E_ALIGN, "a and w must be 16-byte aligned");
+    EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    ep.a_scale = a_scale;
+    ep.w_scale = w_scale;
+    ep.acc_out = acc_out;
+    ep.ldacc = N;
+    RUN(launch_gemm_i8(a, w, M, N, K, ep, S(stream)), "w8a8_linear");
+    return DIT_OK;
+}
+
+int bf16_linear(const void* a, int64_t M, int64_t K, int64_t lda, const void* w, const float* bias,
+                int64_t N, void* y, int y_dtype, int64_t ldy, void* stream) {
+    CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && N >= 1 && lda >= K && ldy >= N, DIT_E_SHAPE, "bad sizes or strides");
+    CHECK(K % 64 == 0 && lda % 8 == 0, DIT_E_UNSUPPORTED, "K must be a multiple of 64, lda of 8");
+    CHECK(N % 16 == 0, DIT_E_UNSUPPORTED, "N must be a multiple of 16");
+    CHECK(((M + 127) / 128) * ((N + 127) / 128) < 0x7fffffff, DIT_E_UNSUPPORTED, "too many tiles");
+    if (M == 0) return DIT_OK;
+    CHECK(a && w && y, DIT_E_NULL, "a, w and y must be non-NULL");
+    CHECK(aligned16(a) && aligned16(w), DIT_E_ALIGN, "a and w must be 16-byte aligned");
+    EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    RUN(launch_gemm_bf16(a, lda, w, M, N, K, ep, S(stream)), "bf16_linear");
+    return DIT_OK;
+}
+
+int f32_linear(const float* a, int64_t M, int64_t K, int64_t lda, const float* w, const float* bias,
+               int64_t N, float* y, int64_t ldy, void* stream) {
+    CHECK(M >= 0 && K >= 1 && N >= 1 && lda >= K && ldy >= N, DIT_E_SHAPE, "bad sizes or strides");
+    CHECK(K % 16 == 0 && N % 16 == 0, DIT_E_UNSUPPORTED, "K and N must be multiples of 16");
+    CHECK((M + 63) / 64 < 65536, DIT_E_UNSUPPORTED, "M too large for the fp32 kernel");
+    if (M == 0) return DIT_OK;
+    CHECK(a && w && y, DIT_E_NULL, "a, w and y must be non-NULL");
+    EpiParams ep = store_epi(y, ldy, false, bias);
+    RUN(launch_gemm_f32(a, lda, w, M, N, K, ep, S(stream)), "f32_linear");
+    return DIT_OK;
+}
+
+int block_causal_attention(const void* q, const void* k, const void* v, void* o, int dtype, int64_t T_q,
+                           int64_t T_k, int32_t H, int32_t d, int64_t ldq, int64_t ldk, int64_t ldv,
+                           int64_t ldo, const int32_t* seg_len, int32_t n_seg, float sm_scale,
+                           void* stream) {
+    CHECK(dtype == DIT_BF16 || dtype == DIT_F32, DIT_E_DTYPE, "dtype must be bf16 or f32");
+    CHECK(d == 128, DIT_E_UNSUPPORTED, "only head_dim 128 is supported (got %d)", d);
+    CHECK(H >= 1 && H <= 65535, DIT_E_SHAPE, "H=%d outside [1, 65535]", H);
+    CHECK(T_q >= 0 && T_q <= T_k, DIT_E_SHAPE, "need 0 <= T_q <= T_k");
+    const int64_t row = (int64_t)H * d;
+    CHECK(ldq >= row && ldk >= row && ldv >= row && ldo >= row, DIT_E_SHAPE, "row strides must be >= H*d");
+    CHECK(ldq % 8 == 0 && ldk % 8 == 0 && ldv % 8 == 0 && ldo % 8 == 0, DIT_E_ALIGN,
+          "row strides must be multiples of 8 elements");
+    CHECK(T_k < ((int64_t)1 << 40), DIT_E_UNSUPPORTED, "T_k too large");
+    int s = check_segs(seg_len, n_seg, T_k);
+    if (s) return s;
+    if (T_q == 0) return DIT_OK;
+    CHECK(q && k && v && o, DIT_E_NULL, "q, k, v and o must be non-NULL");
+    CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(o), DIT_E_ALIGN,
+          "q, k, v and o must be 16-byte aligned");
+    if (sm_scale <= 0.0f) sm_scale = 1.0f / std::sqrt((float)d);
+    const AttnSegs segs = make_attn_segs(seg_len, n_seg);
+    if (dtype == DIT_BF16) {
+        CHECK((T_q + 127) / 128 < 0x7fffffff, DIT_E_UNSUPPORTED, "T_q too large");
+        RUN(launch_attention_bf16(q, k, v, o, T_q, T_k, H, ldq, ldk, ldv, ldo, segs, sm_scale, S(stream)),
+            "attention_bf16");
+    } else {
+        CHECK((T_q * H + 3) / 4 < 0x7fffffff, DIT_E_UNSUPPORTED, "T_q*H too large");
+        RUN(launch_attention_f32((const float*)q, (const float*)k, (const float*)v, (float*)o, T_q, T_k, H,
+                                 ldq, ldk, ldv, ldo, segs, sm_scale, S(stream)),
+            "attention_f32");
+    }
+    return DIT_OK;
+}
+
+int dit_rope_tables(int32_t text_len, const int32_t* grids, int32_t n_img, int64_t row0, int64_t T_rows,
+                    float theta, float* cos_out, float* sin_out, void* stream) {
+    CHECK(text_len >= 0 && n_img >= 0 && n_img <= 15, DIT_E_UNSUPPORTED, "need text_len>=0, 0<=n_img<=15");
+    CHECK(n_img == 0 || grids != nullptr, DIT_E_NULL, "grids is NULL");
+    CHECK(theta > 0.0f, DIT_E_SHAPE, "theta must be positive");
+    int64_t total = text_len;
+    for (int k = 0; k < n_img; ++k) {
+        CHECK(grids[2 * k] >= 1 && grids[2 * k + 1] >= 1, DIT_E_SHAPE, "grid %d has a zero side", k);
+        total += (int64_t)grids[2 * k] * grids[2 * k + 1];
+    }
+    CHECK(row0 >= 0 && T_rows >= 0 && row0 + T_rows <= total, DIT_E_SHAPE, "rows outside the sequence");
+    CHECK(T_rows * 64 / 256 < 0x7fffffff, DIT_E_UNSUPPORTED, "too many rows");
+    if (T_rows == 0) return DIT_OK;
+    CHECK(cos_out && sin_out, DIT_E_NULL, "cos_out and sin_out must be non-NULL");
+    RUN(launch_rope_tables(text_len, grids, n_img, row0, T_rows, theta, cos_out, sin_out, S(stream)),
+        "rope_tables");
+    return DIT_OK;
+}
+
+int dit_qk_norm_rope(const void* qkv, int dtype, int64_t T, int32_t H, const float* g_q, const float* g_k,
+                     const float* cos_t, const float* sin_t, float eps, void* q_out, void* k_out,
+                     int64_t ldk, void* v_out, int64_t ldv, void* stream) {
+    CHECK(dtype == DIT_BF16 || dtype == DIT_F32, DIT_E_DTYPE, "dtype must be bf16 or f32");
+    CHECK(T >= 0 && H >= 1, DIT_E_SHAPE, "need T>=0, H>=1");
+    CHECK(ldk >= (int64_t)H * 128 && ldv >= (int64_t)H * 128, DIT_E_SHAPE, "ldk, ldv must be >= H*128");
+    CHECK(ldk % 2 == 0 && ldv % 2 == 0, DIT_E_ALIGN, "ldk, ldv must be even");
+    CHECK((T * H + 3) / 4 < 0x7fffffff, DIT_E_UNSUPPORTED, "T*H too large");
+    if (T == 0) return DIT_OK;
+    CHECK(qkv && g_q && g_k && cos_t && sin_t && q_out && k_out && v_out, DIT_E_NULL, "NULL argument");
+    RUN(launch_qk_norm_rope(qkv, dtype == DIT_BF16, T, H, g_q, g_k, cos_t, sin_t, eps, q_out, k_out, ldk,
+                            v_out, ldv, S(stream)),
+        "qk_norm_rope");
+    return DIT_OK;
+}
+
+int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const float* shift,
+                       const float* scale, float eps, void* h_out, int h_dtype, int8_t* q_out,
+                       float* q_scale, void* stream) {
+    CHECK(x_dtype == DIT_BF16 || x_dtype == DIT_F32, DIT_E_DTYPE, "x_dtype must be bf16 or f32");
+    CHECK(q_out != nullptr || h_dtype == x_dtype, DIT_E_DTYPE, "h_dtype must equal x_dtype");
+    CHECK(M >= 0 && D >= 256, DIT_E_SHAPE, "need M>=0, D>=256");
+    CHECK(D % 256 == 0 && D <= 8192, DIT_E_UNSUPPORTED, "D must be a multiple of 256, <= 8192");
+    CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
+    if (M == 0) return DIT_OK;
+    CHECK(x && shift && scale, DIT_E_NULL, "x, shift and scale must be non-NULL");
+    CHECK(q_out ? (q_scale != nullptr) : (h_out != nullptr), DIT_E_NULL, "output pointer is NULL");
+    CHECK(aligned16(x) && (!q_out || aligned16(q_out)), DIT_E_ALIGN, "x and q_out must be 16-byte aligned");
+    SegMap sm{};
+    sm.end[0] = M;
+    sm.set[0] = 0;
+    sm.n = 1;
+    RUN(launch_adaln(x, x_dtype == DIT_BF16, M, D, shift, scale, 0, sm, eps, h_out, q_out, q_scale, S(stream)),
+        "adaln");
+    return DIT_OK;
+}
+
+int dit_euler_step(float* x, const void* v, int v_dtype, int64_t n, float sigma, float sigma_next,
+                   void* stream) {
+    CHECK(v_dtype == DIT_BF16 || v_dtype == DIT_F32, DIT_E_DTYPE, "v_dtype must be bf16 or f32");
+    CHECK(n >= 0 && (n + 255) / 256 < 0x7fffffff, DIT_E_SHAPE, "bad n");
+    if (n == 0) return DIT_OK;
+    CHECK(x && v, DIT_E_NULL, "x and v must be non-NULL");
+    RUN(launch_euler(x, v, v_dtype == DIT_BF16, n, sigma, sigma_next, S(stream)), "euler");
+    return DIT_OK;
+}
+
+int dit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* stream) {
+    CHECK((x_dtype == DIT_BF16 || x_dtype == DIT_F32) && (y_dtype == DIT_BF16 || y_dtype == DIT_F32), DIT_E_DTYPE,
+          "dtypes must be bf16 or f32");
+    CHECK(n >= 0 && (n + 255) / 256 < 0x7fffffff, DIT_E_SHAPE, "bad n");
+    if (n == 0) return DIT_OK;
+    CHECK(x && y, DIT_E_NULL, "x and y must be non-NULL");
+    RUN(launch_cast(x, x_dtype == DIT_BF16, y, y_dtype == DIT_BF16, n, S(stream)), "cast");
+    return DIT_OK;
+}
+
+// ------------------------------------------------------------------ block
+
+namespace {
+
+struct Plan {
+    size_t h, a8, sa, qkv, q, o, o8, so, g, g8, sg, total;
+};
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
+Plan plan(const dit_block_config* cfg, int64_t T) {
+    const size_t act = cfg->mode == DIT_MODE_F32 ? 4 : 2;
+    const size_t D = cfg->D, F = cfg->F;
+    const bool q8 = cfg->mode == DIT_MODE_W8A8;
+    Plan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += up256(bytes);
+        return at;
+    };
+    p.h = take(q8 ? 0 : T * D * act);
+    p.a8 = take(q8 ? T * D : 0);
+    p.sa = take(q8 ? T * 4 : 0);
+    p.qkv = take(T * 3 * D * act);
+    p.q = take(T * D * act);
+    p.o = take(T * D * act);
+    p.o8 = take(q8 ? T * D : 0);
+    p.so = take(q8 ? T * 4 : 0);
+    p.g = take(T * F * act);
+    p.g8 = take(q8 ? T * F : 0);
+    p.sg = take(q8 ? T * 4 : 0);
+    p.total = off;
+    return p;
+}
+
+int check_cfg(const dit_block_config* cfg) {
+    CHECK(cfg != nullptr, DIT_E_NULL, "cfg is NULL");
+    CHECK(cfg->mode >= DIT_MODE_F32 && cfg->mode <= DIT_MODE_W8A8, DIT_E_DTYPE, "unknown mode %d", cfg->mode);
+    CHECK(cfg->head_dim == 128, DIT_E_UNSUPPORTED, "head_dim must be 128");
+    CHECK(cfg->H >= 1 && (int64_t)cfg->D == (int64_t)cfg->H * 128, DIT_E_SHAPE, "D must equal H*128");
+    CHECK(cfg->D % 256 == 0 && cfg->D <= 8192, DIT_E_UNSUPPORTED, "D must be a multiple of 256, <= 8192");
+    CHECK(cfg->F >= 256 && cfg->F % 256 == 0 && cfg->F <= 16384, DIT_E_UNSUPPORTED,
+          "F must be a multiple of 256 in [256, 16384]");
+    CHECK(cfg->ln_eps >= 0.0f && cfg->qk_eps >= 0.0f, DIT_E_SHAPE, "eps must be >= 0");
+    return DIT_OK;
+}
+
+int check_weights(const dit_block_config* cfg, const dit_block_weights* w) {
+    CHECK(w != nullptr, DIT_E_NULL, "weights is NULL");
+    CHECK(w->w_qkv && w->w_o && w->w_1 && w->w_2, DIT_E_NULL, "a weight matrix is NULL");
+    CHECK(w->b_qkv && w->b_o && w->b_1 && w->b_2, DIT_E_NULL, "a bias is NULL");
+    CHECK(w->g_q && w->g_k, DIT_E_NULL, "g_q or g_k is NULL");
+    if (cfg->mode == DIT_MODE_W8A8)
+        CHECK(w->s_qkv && w->s_o && w->s_1 && w->s_2, DIT_E_NULL, "W8A8 needs the weight scales");
+    CHECK(aligned16(w->w_qkv) && aligned16(w->w_o) && aligned16(w->w_1) && aligned16(w->w_2), DIT_E_ALIGN,
+          "weights must be 16-byte aligned");
+    return DIT_OK;
+}
+
+int check_io(const dit_block_config* cfg, const dit_block_io* io) {
+    CHECK(io != nullptr, DIT_E_NULL, "io is NULL");
+    CHECK(io->T_q >= 0 && io->T_q <= io->T_k, DIT_E_SHAPE, "need 0 <= T_q <= T_k");
+    CHECK(io->T_k <= ((int64_t)1 << 31), DIT_E_UNSUPPORTED, "T_k too large");
+    int s = check_segs(io->seg_len, io->n_seg, io->T_k);
+    if (s) return s;
+    CHECK(io->n_mod >= 1, DIT_E_SHAPE, "n_mod must be >= 1");
+    CHECK(io->mod_of_seg != nullptr, DIT_E_NULL, "mod_of_seg is NULL");
+    for (int i = 0; i < io->n_seg; ++i)
+        CHECK(io->mod_of_seg[i] >= 0 && io->mod_of_seg[i] < io->n_mod, DIT_E_SHAPE,
+              "mod_of_seg[%d]=%d outside [0, n_mod)", i, io->mod_of_seg[i]);
+    if (io->T_q == 0) return DIT_OK;
+    CHECK(io->x && io->mod && io->cos_t && io->sin_t && io->k_cache && io->v_cache, DIT_E_NULL,
+          "x, mod, cos_t, sin_t, k_cache and v_cache must be non-NULL");
+    CHECK(aligned16(io->x) && aligned16(io->k_cache) && aligned16(io->v_cache), DIT_E_ALIGN,
+          "x and the caches must be 16-byte aligned");
+    (void)cfg;
+    return DIT_OK;
+}
+
+int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const dit_block_io* io,
+               void* k_cache, void* v_cache, uint8_t* ws, hipStream_t st) {
+    const int64_t T = io->T_q, D = cfg->D, F = cfg->F;
+    const int H = cfg->H;
+    const int mode = cfg->mode;
+    const bool f32 = mode == DIT_MODE_F32, q8 = mode == DIT_MODE_W8A8;
+    const bool bf = !f32;
+    const size_t act = f32 ? 4 : 2;
+    const Plan p = plan(cfg, T);
+    const int64_t row_off = io->T_k - io->T_q;
+    const SegMap sm = make_segmap(io->seg_len, io->mod_of_seg, io->n_seg, row_off);
+    const AttnSegs segs = make_attn_segs(io->seg_len, io->n_seg);
+    const int64_t mstride = 6 * D;
+    void* x = io->x;
+    void* h = ws + p.h;
+    int8_t* a8 = (int8_t*)(ws + p.a8);
+    float* sa = (float*)(ws + p.sa);
+    void* qkv = ws + p.qkv;
+    void* qb = ws + p.q;
+    void* ob = ws + p.o;
+    int8_t* o8 = (int8_t*)(ws + p.o8);
+    float* so = (float*)(ws + p.so);
+    void* gb = ws + p.g;
+    int8_t* g8 = (int8_t*)(ws + p.g8);
+    float* sg = (float*)(ws + p.sg);
+    uint8_t* kc = (uint8_t*)k_cache + (size_t)row_off * D * act;
+    uint8_t* vc = (uint8_t*)v_cache + (size_t)row_off * D * act;
+
+    auto gemm = [&](const void* A, const int8_t* A8, const float* As, const void* Wt, const float* Ws,
+                    int64_t N, int64_t K, const EpiParams& ep) -> hipError_t {
+        if (q8) {
+            EpiParams e = ep;
+            e.a_scale = As;
+            e.w_scale = Ws;
+            return launch_gemm_i8(A8, (const int8_t*)Wt, T, N, K, e, st);
+        }
+        if (bf) return launch_gemm_bf16(A, K, Wt, T, N, K, ep, st);
+        return launch_gemm_f32((const float*)A, K, (const float*)Wt, T, N, K, ep, st);
+    };
+
+    // S1: adaLN prologue 1 (fused per-token quantization in W8A8 mode)
+    RUN(launch_adaln(x, bf, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
+        "adaln1");
+    // S2: QKV linear -> qkv (bf16-rounded in bf16 modes)
+    {
+        EpiParams ep = store_epi(qkv, 3 * D, bf, w->b_qkv);
+        RUN(gemm(h, a8, sa, w->w_qkv, w->s_qkv, 3 * D, D, ep), "qkv_gemm");
+    }
+    // S3: Q/K RMSNorm + RoPE, K/V rows into the cache
+    RUN(launch_qk_norm_rope(qkv, bf, T, H, w->g_q, w->g_k, io->cos_t, io->sin_t, cfg->qk_eps, qb, kc, D, vc,
+                            D, st),
+        "qk_norm_rope");
+    // S4: block-causal attention over the whole cache
+    const float scale = 1.0f / std::sqrt(128.0f);
+    if (bf)
+        RUN(launch_attention_bf16(qb, k_cache, v_cache, ob, T, io->T_k, H, D, D, D, D, segs, scale, st),
+            "attention");
+    else
+        RUN(launch_attention_f32((const float*)qb, (const float*)k_cache, (const float*)v_cache, (float*)ob, T,
+                                 io->T_k, H, D, D, D, D, segs, scale, st),
+            "attention");
+    // S5 + S6: quantize o, out-projection with gated residual into x
+    if (q8) RUN(launch_quantize_rows(ob, true, T, D, D, o8, so, st), "quantize_o");
+    {
+        EpiParams ep{};
+        ep.kind = EPI_RESID;
+        ep.act_bf16 = bf;
+        ep.bias = w->b_o;
+        ep.x = x;
+        ep.ldx = D;
+        ep.gate = io->mod + 2 * D;
+        ep.gate_stride = mstride;
+        ep.sm = sm;
+        RUN(gemm(ob, o8, so, w->w_o, w->s_o, D, D, ep), "out_gemm");
+    }
+    // S7: adaLN prologue 2
+    RUN(launch_adaln(x, bf, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
+        "adaln2");
+    // S8: MLP up + GELU
+    {
+        EpiParams ep{};
+        ep.kind = EPI_GELU;
+        ep.act_bf16 = bf;
+        ep.y_bf16 = bf;
+        ep.bias = w->b_1;
+        ep.y = gb;
+        ep.ldy = F;
+        RUN(gemm(h, a8, sa, w->w_1, w->s_1, F, D, ep), "up_gemm");
+    }
+    // S9 + S10: quantize g, MLP down with gated residual into x
+    if (q8) RUN(launch_quantize_rows(gb, true, T, F, F, g8, sg, st), "quantize_g");
+    {
+        EpiParams ep{};
+        ep.kind = EPI_RESID;
+        ep.act_bf16 = bf;
+        ep.bias = w->b_2;
+        ep.x = x;
+        ep.ldx = D;
+        ep.gate = io->mod + 5 * D;
+        ep.gate_stride = mstride;
+        ep.sm = sm;
+        RUN(gemm(gb, g8, sg, w->w_2, w->s_2, D, F, ep), "down_gemm");
+    }
+    return DIT_OK;
+}
+
+}  // namespace
+
+size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k) {
+    (void)T_k;
+    if (!cfg || T_q < 0) return 0;
+    return plan(cfg, T_q).total;
+}
+
+int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w, const dit_block_io* io,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_cfg(cfg);
+    if (s) return s;
+    s = check_weights(cfg, w);
+    if (s) return s;
+    s = check_io(cfg, io);
+    if (s) return s;
+    if (io->T_q == 0) return DIT_OK;
+    const size_t need = plan(cfg, io->T_q).total;
+    CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
+    CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
+    return block_impl(cfg, w, io, io->k_cache, io->v_cache, (uint8_t*)workspace, S(stream));
+}
+
+int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weights, int32_t n_blocks,
+                      const dit_block_io* io, void* const* k_caches, void* const* v_caches, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    int s = check_cfg(cfg);
+    if (s) return s;
+    CHECK(n_blocks >= 0 && (n_blocks == 0 || weights != nullptr), DIT_E_NULL, "weights is NULL");
+    CHECK(k_caches != nullptr && v_caches != nullptr, DIT_E_NULL, "cache arrays are NULL");
+    for (int b = 0; b < n_blocks; ++b) {
+        s = check_weights(cfg, &weights[b]);
+        if (s) return s;
+        CHECK(k_caches[b] && v_caches[b], DIT_E_NULL, "cache of block %d is NULL", b);
+        CHECK(aligned16(k_caches[b]) && aligned16(v_caches[b]), DIT_E_ALIGN, "caches must be 16-byte aligned");
+    }
+    dit_block_io one = *io;
+    one.k_cache = n_blocks ? k_caches[0] : io->k_cache;
+    one.v_cache = n_blocks ? v_caches[0] : io->v_cache;
+    s = check_io(cfg, &one);
+    if (s) return s;
+    if (io->T_q == 0 || n_blocks == 0) return DIT_OK;
+    const size_t need = plan(cfg, io->T_q).total;
+    CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
+    CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
+    for (int b = 0; b < n_blocks; ++b) {
+        s = block_impl(cfg, &weights[b], io, k_caches[b], v_caches[b], (uint8_t*)workspace, S(stream));
+        if (s) return s;
+    }
+    return DIT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// Block-causal flash attention, head dim 128.
+//
+// Block-causal structure: segments are consecutive key ranges and a query of
+// segment s sees segments 0..s, i.e. exactly the key prefix [0, end(s)).  A
+// workgroup of 128 queries therefore loops over keys [0, end of its last
+// query's segment) and masks only the tiles that cross the first query's
+// segment end; fully masked tiles are never visited.
+//
+// bf16 kernel (gfx950 MFMA 32x32x16 bf16): 4 waves x 32 queries.  Each wave
+// computes S^T = K Q^T so that every lane owns one query column: the row max
+// and row sum of the online softmax are lane-local except for one exchange
+// between lane l and lane l^32.  O^T = V^T P^T accumulates in 64 fp32
+// registers per lane.  K tiles sit in LDS key-major, V tiles transposed
+// (d-major), both padded for conflict-free reads.  The PV product uses a
+// fixed permutation of the 16 keys of each MFMA step (the order in which the
+// S^T accumulator hands them to a lane), applied to both operands.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+constexpr int AQ = 128;                 // queries per workgroup
+constexpr int AK = 64;                  // keys per tile
+constexpr int KS_STRIDE = 128 * 2 + 16; // bytes per key row of the K tile
+constexpr int VT_STRIDE = AK * 2 + 8;   // bytes per d row of the transposed V tile
+
+__device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
+    int s = 0;
+#pragma unroll 1
+    for (; s < sg.n - 1; ++s)
+        if (pos < sg.end[s]) break;
+    return sg.end[s];
+}
+
+__global__ void __launch_bounds__(256, 2)
+attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
+                 const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int64_t T_q, int64_t T_k,
+                 int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, AttnSegs sg, float c_log2) {
+    __shared__ __attribute__((aligned(16))) uint8_t Ks[AK * KS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint8_t Vt[128 * VT_STRIDE];
+
+    const int nqb = (int)((T_q + AQ - 1) / AQ);
+    const int qb = nqb - 1 - (int)blockIdx.x;   // longest key ranges first
+    const int h = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int hh = lane / 32, lq = lane % 32;
+    const int64_t off = T_k - T_q;
+
+    const int64_t q_first = (int64_t)qb * AQ;
+    const int64_t q_last = min(q_first + AQ, T_q) - 1;
+    const int64_t kv_min = kv_end_of(sg, off + q_first);
+    const int64_t kv_hi = kv_end_of(sg, off + q_last);
+
+    const int64_t qi = q_first + wave * 32 + lq;   // this lane's query
+    const bool q_ok = qi < T_q;
+    const int64_t my_end = q_ok ? kv_end_of(sg, off + qi) : T_k;
+
+    // Q^T fragments (B operand): Q[qi][kb*16 + hh*8 .. +7]
+    v8bf qf[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        if (q_ok)
+            qf[kb] = *reinterpret_cast<const v8bf*>(Q + qi * ldq + (int64_t)h * 128 + kb * 16 + hh * 8);
+        else
+            qf[kb] = v8bf{};
+    }
+
+    v16f oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = v16f{};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    const int ntiles = (int)((kv_hi + AK - 1) / AK);
+    for (int t = 0; t < ntiles; ++t) {
+        const int64_t j0 = (int64_t)t * AK;
+        __syncthreads();
+        // K tile: 64 keys x 256 bytes, 16-byte chunks
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int c = tid + i * 256;
+            const int key = c / 16, ch = c % 16;
+            const int64_t gk = j0 + key;
+            uint4 val = make_uint4(0, 0, 0, 0);
+            if (gk < T_k) val = *reinterpret_cast<const uint4*>(Kg + gk * ldk + (int64_t)h * 128 + ch * 8);
+            *reinterpret_cast<uint4*>(&Ks[key * KS_STRIDE + ch * 16]) = val;
+        }
+        // V tile transposed: thread owns d-chunk dc (8 dims) of keys 4kg..4kg+3
+        {
+            const int dc = tid % 16, kg = tid / 16;
+            uint4 rv[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t gk = j0 + kg * 4 + i;
+                rv[i] = gk < T_k ? *reinterpret_cast<const uint4*>(Vg + gk * ldv + (int64_t)h * 128 + dc * 8)
+                                 : make_uint4(0, 0, 0, 0);
+            }
+            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
+            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&rv[1]);
+            const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&rv[2]);
+            const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&rv[3]);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                uint2 packed;
+                packed.x = (uint32_t)e0[r] | ((uint32_t)e1[r] << 16);
+                packed.y = (uint32_t)e2[r] | ((uint32_t)e3[r] << 16);
+                *reinterpret_cast<uint2*>(&Vt[(dc * 8 + r) * VT_STRIDE + kg * 8]) = packed;
+            }
+        }
+        __syncthreads();
+
+        // S^T = K Q^T : two 32-key halves
+        v16f sacc[2];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+            sacc[kh] = v16f{};
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb) {
+                const v8bf a = *reinterpret_cast<const v8bf*>(
+                    &Ks[(kh * 32 + lq) * KS_STRIDE + kb * 32 + hh * 16]);
+                sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], sacc[kh], 0, 0, 0);
+            }
+        }
+        // mask keys beyond this query's visible prefix (only tiles that cross it)
+        if (j0 + AK > kv_min) {
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int64_t key = j0 + kh * 32 + (j / 4) * 8 + hh * 4 + (j % 4);
+                    if (key >= my_end) sacc[kh][j] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f((m_run - m_new) * c_log2);
+        const float mb = m_new * c_log2;
+        float psum = 0.0f;
+        v8bf pb[4];
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const float p = exp2f(fmaf(sacc[kh][j], c_log2, -mb));
+                psum += p;
+                pb[kh * 2 + j / 8][j % 8] = to_bf16(p);
+            }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+
+        // O^T += V^T P^T, 16 keys per MFMA in the S^T lane order
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint8_t* row = &Vt[(dt * 32 + lq) * VT_STRIDE];
+                const uint2 lo = *reinterpret_cast<const uint2*>(row + (16 * b + hh * 4) * 2);
+                const uint2 hi = *reinterpret_cast<const uint2*>(row + (16 * b + 8 + hh * 4) * 2);
+                uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<v8bf*>(&av), pb[b],
+                                                                   oacc[dt], 0, 0, 0);
+            }
+        }
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
+    if (!q_ok) return;
+    const float inv = 1.0f / l_tot;
+    __bf16* orow = O + qi * ldo + (int64_t)h * 128;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            v4bf outv;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) outv[r] = to_bf16(oacc[dt][g * 4 + r] * inv);
+            *reinterpret_cast<v4bf*>(orow + dt * 32 + g * 8 + hh * 4) = outv;
+        }
+}
+
+hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, int64_t T_q,
+                                 int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
+                                 int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st) {
+    if (T_q == 0) return hipSuccess;
+    const float c = sm_scale * 1.4426950408889634f;
+    dim3 grid((unsigned)((T_q + AQ - 1) / AQ), (unsigned)H);
+    attn_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
+                                           (__bf16*)o, T_q, T_k, ldq, ldk, ldv, ldo, segs, c);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fp32 (fp32 mode)
+// One wave per (query, head); lane l holds dims 2l, 2l+1.  Plain online softmax
+// over the visible key prefix.
+__global__ void __launch_bounds__(256) attn_f32_kernel(const float* __restrict__ Q,
+                                                       const float* __restrict__ Kg,
+                                                       const float* __restrict__ Vg,
+                                                       float* __restrict__ O, int64_t T_q,
+                                                       int64_t T_k, int H, int64_t ldq, int64_t ldk,
+                                                       int64_t ldv, int64_t ldo, AttnSegs sg,
+                                                       float scale) {
+    const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (item >= T_q * H) return;
+    const int lane = threadIdx.x % kWave;
+    const int64_t i = item / H;
+    const int h = (int)(item % H);
+    const int64_t end = kv_end_of(sg, T_k - T_q + i);
+    const float q0 = Q[i * ldq + h * 128 + 2 * lane], q1 = Q[i * ldq + h * 128 + 2 * lane + 1];
+    float m = -INFINITY, l = 0.0f, o0 = 0.0f, o1 = 0.0f;
+    for (int64_t j = 0; j < end; ++j) {
+        const float* kr = Kg + j * ldk + h * 128 + 2 * lane;
+        const float s = wave_sum(q0 * kr[0] + q1 * kr[1]) * scale;
+        const float m_new = fmaxf(m, s);
+        const float a = expf(m - m_new), p = expf(s - m_new);
+        const float* vr = Vg + j * ldv + h * 128 + 2 * lane;
+        o0 = o0 * a + p * vr[0];
+        o1 = o1 * a + p * vr[1];
+        l = l * a + p;
+        m = m_new;
+    }
+    O[i * ldo + h * 128 + 2 * lane] = o0 / l;
+    O[i * ldo + h * 128 + 2 * lane + 1] = o1 / l;
+}
+
+hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, int64_t T_q,
+                                int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
+                                int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st) {
+    const int64_t items = T_q * H;
+    if (items == 0) return hipSuccess;
+    attn_f32_kernel<<<(unsigned)((items + 3) / 4), 256, 0, st>>>(q, k, v, o, T_q, T_k, H, ldq, ldk, ldv,
+                                                                 ldo, segs, sm_scale);
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,88 @@
+// Shared device helpers for the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dit {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxSeg = 16;
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
+__device__ __forceinline__ float bf16r(float f) { return (float)(__bf16)f; }
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<__bf16>(__bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ __bf16 from_f<__bf16>(float v) { return (__bf16)v; }
+
+// Round to the storage precision of the mode: identity for fp32, bf16 otherwise.
+template <typename T> __device__ __forceinline__ float store_round(float v);
+template <> __device__ __forceinline__ float store_round<float>(float v) { return v; }
+template <> __device__ __forceinline__ float store_round<__bf16>(float v) { return bf16r(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+
+// Block-wide reduction over `nwaves` waves through a small LDS array.
+template <int NWAVES, bool MAX>
+__device__ __forceinline__ float block_reduce(float v, float* red) {
+    v = MAX ? wave_max(v) : wave_sum(v);
+    const int w = threadIdx.x / kWave, l = threadIdx.x % kWave;
+    __syncthreads();
+    if (l == 0) red[w] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int i = 1; i < NWAVES; ++i) r = MAX ? fmaxf(r, red[i]) : r + red[i];
+    return r;
+}
+
+// Row -> modulation set lookup.  Segments are consecutive ranges of the
+// sequence; row r of a call sits at absolute position row_offset + r.
+struct SegMap {
+    int64_t end[kMaxSeg];   // absolute end position of each segment
+    int32_t set[kMaxSeg];   // modulation set of each segment
+    int32_t n;
+    int64_t row_offset;
+};
+
+__device__ __forceinline__ int seg_set(const SegMap& sm, int64_t row) {
+    const int64_t p = sm.row_offset + row;
+    int s = 0;
+#pragma unroll 1
+    for (; s < sm.n - 1; ++s)
+        if (p < sm.end[s]) break;
+    return sm.set[s];
+}
+
+// Symmetric int8 code of v for scale s (s == 0 -> 0); IEEE fp32 division,
+// ties to even.
+__device__ __forceinline__ int8_t quant_code(float v, float s) {
+    if (s == 0.0f) return 0;
+    float r = rintf(__fdiv_rn(v, s));
+    r = fminf(fmaxf(r, -127.0f), 127.0f);
+    return (int8_t)(int)r;
+}
+
+}  // namespace dit

@@ -1,0 +1,405 @@
+// HBM-bound kernels of the block: per-row int8 quantization, the adaLN
+// prologue (optionally fused with quantization), Q/K RMSNorm + RoPE with the
+// K/V cache write, RoPE tables and the Euler update.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+// ---------------------------------------------------------------- quantization
+// One 256-thread workgroup per row.  The row is read once into registers as
+// 16-byte chunks (8 bf16 or 4 f32 values), reduced to amax, then coded.
+template <typename T, int MAXC>
+__global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict__ x, int64_t K,
+                                                            int64_t ldx, int8_t* __restrict__ q,
+                                                            float* __restrict__ scale) {
+    constexpr int E = 16 / sizeof(T);   // values per 16-byte chunk
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const T* xr = x + row * ldx;
+    const int nchunk = (int)(K / E);
+    uint4 buf[MAXC];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + i * 256;
+        if (c < nchunk) {
+            buf[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * E);
+            const T* v = reinterpret_cast<const T*>(&buf[i]);
+#pragma unroll
+            for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(to_f<T>(v[e])));
+        }
+    }
+    amax = block_reduce<4, true>(amax, red);
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (threadIdx.x == 0) scale[row] = s;
+    int8_t* qr = q + row * K;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = threadIdx.x + i * 256;
+        if (c < nchunk) {
+            const T* v = reinterpret_cast<const T*>(&buf[i]);
+            int8_t out[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) out[e] = quant_code(to_f<T>(v[e]), s);
+            if constexpr (E == 8) {
+                *reinterpret_cast<uint2*>(qr + (int64_t)c * E) = *reinterpret_cast<uint2*>(out);
+            } else {
+                *reinterpret_cast<uint32_t*>(qr + (int64_t)c * E) = *reinterpret_cast<uint32_t*>(out);
+            }
+        }
+    }
+}
+
+hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
+                                int8_t* q, float* scale, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (bf16) {
+        const int nchunk = (int)(K / 8);
+        if (nchunk <= 256 * 4)
+            quantize_rows_kernel<__bf16, 4><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const __bf16*)x, K, ldx, q, scale);
+        else
+            quantize_rows_kernel<__bf16, 16><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const __bf16*)x, K, ldx, q, scale);
+    } else {
+        const int nchunk = (int)(K / 4);
+        if (nchunk <= 256 * 4)
+            quantize_rows_kernel<float, 4><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const float*)x, K, ldx, q, scale);
+        else
+            quantize_rows_kernel<float, 16><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const float*)x, K, ldx, q, scale);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- adaLN
+// h = LN(x) * (1 + scale) + shift per row; row r uses modulation set
+// seg_set(r): shift = mod + set*mod_stride, scale = shift + D.  Output either
+// h (bf16-rounded in the bf16 modes) or its int8 codes + per-row scale.
+template <typename T, int VPT>
+__global__ void __launch_bounds__(256) adaln_kernel(const T* __restrict__ x, int64_t D,
+                                                    const float* __restrict__ shift0,
+                                                    const float* __restrict__ scale0,
+                                                    int64_t mod_stride, SegMap sm, float eps,
+                                                    T* __restrict__ h, int8_t* __restrict__ qo,
+                                                    float* __restrict__ qs) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const T* xr = x + row * D;
+    const int set = seg_set(sm, row);
+    const float* shift = shift0 + (int64_t)set * mod_stride;
+    const float* scl = scale0 + (int64_t)set * mod_stride;
+    const int nvec = (int)(D / (256 * 8));   // 8 values per thread per vector step
+    float v[VPT];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT / 8; ++i) {
+        if (i < nvec) {
+            const int64_t c = ((int64_t)i * 256 + threadIdx.x) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[i * 8 + e] = to_f<T>(xr[c + e]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s += v[i * 8 + e];
+        }
+    }
+    const float mean = block_reduce<4, false>(s, red) / (float)D;
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT / 8; ++i)
+        if (i < nvec)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = v[i * 8 + e] - mean;
+                ss += d * d;
+            }
+    const float var = block_reduce<4, false>(ss, red) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < VPT / 8; ++i)
+        if (i < nvec) {
+            const int64_t c = ((int64_t)i * 256 + threadIdx.x) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float hv = store_round<T>((v[i * 8 + e] - mean) * rstd * (1.0f + scl[c + e]) + shift[c + e]);
+                v[i * 8 + e] = hv;
+                amax = fmaxf(amax, fabsf(hv));
+            }
+        }
+    if (qo == nullptr) {
+#pragma unroll
+        for (int i = 0; i < VPT / 8; ++i)
+            if (i < nvec) {
+                const int64_t c = ((int64_t)i * 256 + threadIdx.x) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) h[row * D + c + e] = from_f<T>(v[i * 8 + e]);
+            }
+        return;
+    }
+    amax = block_reduce<4, true>(amax, red);
+    const float sc = __fdiv_rn(amax, 127.0f);
+    if (threadIdx.x == 0) qs[row] = sc;
+#pragma unroll
+    for (int i = 0; i < VPT / 8; ++i)
+        if (i < nvec) {
+            const int64_t c = ((int64_t)i * 256 + threadIdx.x) * 8;
+            int8_t out[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) out[e] = quant_code(v[i * 8 + e], sc);
+            *reinterpret_cast<uint2*>(qo + row * D + c) = *reinterpret_cast<uint2*>(out);
+        }
+}
+
+hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
+                        const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
+                        float* qs, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    // D % 2048 != 0 (e.g. 512) is handled by VPT=8 with nvec = D/2048 == 0 -> use
+    // the scalar-tail variant below.
+    if (D % 2048 == 0) {
+        if (bf16)
+            adaln_kernel<__bf16, 32><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const __bf16*)x, D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs);
+        else
+            adaln_kernel<float, 32><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+                (const float*)x, D, shift, scale, mod_stride, sm, eps, (float*)h, qo, qs);
+    } else {
+        return launch_adaln_small(x, bf16, M, D, shift, scale, mod_stride, sm, eps, h, qo, qs, st);
+    }
+    return hipGetLastError();
+}
+
+// D not a multiple of 2048 (the tiny 512-wide case): one value per thread per step.
+template <typename T>
+__global__ void __launch_bounds__(256) adaln_small_kernel(const T* __restrict__ x, int64_t D,
+                                                          const float* __restrict__ shift0,
+                                                          const float* __restrict__ scale0,
+                                                          int64_t mod_stride, SegMap sm, float eps,
+                                                          T* __restrict__ h, int8_t* __restrict__ qo,
+                                                          float* __restrict__ qs) {
+    __shared__ float red[4];
+    const int64_t row = blockIdx.x;
+    const T* xr = x + row * D;
+    const int set = seg_set(sm, row);
+    const float* shift = shift0 + (int64_t)set * mod_stride;
+    const float* scl = scale0 + (int64_t)set * mod_stride;
+    constexpr int MAXV = 32;
+    float v[MAXV];
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int64_t c = (int64_t)i * 256 + threadIdx.x;
+        v[i] = c < D ? to_f<T>(xr[c]) : 0.0f;
+        s += v[i];
+    }
+    const float mean = block_reduce<4, false>(s, red) / (float)D;
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int64_t c = (int64_t)i * 256 + threadIdx.x;
+        if (c < D) ss += (v[i] - mean) * (v[i] - mean);
+    }
+    const float var = block_reduce<4, false>(ss, red) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int64_t c = (int64_t)i * 256 + threadIdx.x;
+        if (c < D) {
+            v[i] = store_round<T>((v[i] - mean) * rstd * (1.0f + scl[c]) + shift[c]);
+            amax = fmaxf(amax, fabsf(v[i]));
+        }
+    }
+    if (qo == nullptr) {
+#pragma unroll
+        for (int i = 0; i < MAXV; ++i) {
+            const int64_t c = (int64_t)i * 256 + threadIdx.x;
+            if (c < D) h[row * D + c] = from_f<T>(v[i]);
+        }
+        return;
+    }
+    amax = block_reduce<4, true>(amax, red);
+    const float sc = __fdiv_rn(amax, 127.0f);
+    if (threadIdx.x == 0) qs[row] = sc;
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i) {
+        const int64_t c = (int64_t)i * 256 + threadIdx.x;
+        if (c < D) qo[row * D + c] = quant_code(v[i], sc);
+    }
+}
+
+hipError_t launch_adaln_small(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
+                              const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
+                              float* qs, hipStream_t st) {
+    if (bf16)
+        adaln_small_kernel<__bf16><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+            (const __bf16*)x, D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs);
+    else
+        adaln_small_kernel<float><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+            (const float*)x, D, shift, scale, mod_stride, sm, eps, (float*)h, qo, qs);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Q/K RMSNorm + RoPE
+// One wave per (token, head); lane l holds head dims 2l and 2l+1, i.e. RoPE
+// pair l, so the rotation is lane-local and the RMS is one wave reduction.
+template <typename T>
+__device__ __forceinline__ void norm_rope_pair(float a, float b, float g0, float g1, float c,
+                                               float s, float eps, float& oa, float& ob) {
+    const float ms = wave_sum(a * a + b * b) * (1.0f / 128.0f);
+    const float r = 1.0f / sqrtf(ms + eps);
+    // cast to the gain's dtype before the gain multiply, then round the product
+    const float na = store_round<T>(store_round<T>(a * r) * g0);
+    const float nb = store_round<T>(store_round<T>(b * r) * g1);
+    oa = store_round<T>(na * c - nb * s);
+    ob = store_round<T>(na * s + nb * c);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) qk_norm_rope_kernel(
+    const T* __restrict__ qkv, int64_t T_rows, int H, const float* __restrict__ g_q,
+    const float* __restrict__ g_k, const float* __restrict__ cos_t, const float* __restrict__ sin_t,
+    float eps, T* __restrict__ q_out, T* __restrict__ k_out, int64_t ldk, T* __restrict__ v_out,
+    int64_t ldv) {
+    const int64_t item = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (item >= T_rows * H) return;
+    const int lane = threadIdx.x % kWave;
+    const int64_t t = item / H;
+    const int h = (int)(item % H);
+    const int64_t D = (int64_t)H * 128;
+    const T* row = qkv + t * 3 * D + h * 128 + 2 * lane;
+    const float c = cos_t[t * 64 + lane], s = sin_t[t * 64 + lane];
+    const float gq0 = g_q[2 * lane], gq1 = g_q[2 * lane + 1];
+    const float gk0 = g_k[2 * lane], gk1 = g_k[2 * lane + 1];
+    float a, b;
+    norm_rope_pair<T>(to_f<T>(row[0]), to_f<T>(row[1]), gq0, gq1, c, s, eps, a, b);
+    T* qo = q_out + t * D + h * 128 + 2 * lane;
+    qo[0] = from_f<T>(a);
+    qo[1] = from_f<T>(b);
+    norm_rope_pair<T>(to_f<T>(row[D]), to_f<T>(row[D + 1]), gk0, gk1, c, s, eps, a, b);
+    T* ko = k_out + t * ldk + h * 128 + 2 * lane;
+    ko[0] = from_f<T>(a);
+    ko[1] = from_f<T>(b);
+    T* vo = v_out + t * ldv + h * 128 + 2 * lane;
+    vo[0] = row[2 * D];
+    vo[1] = row[2 * D + 1];
+}
+
+hipError_t launch_qk_norm_rope(const void* qkv, bool bf16, int64_t T, int H, const float* g_q,
+                               const float* g_k, const float* cos_t, const float* sin_t, float eps,
+                               void* q_out, void* k_out, int64_t ldk, void* v_out, int64_t ldv,
+                               hipStream_t st) {
+    const int64_t items = T * H;
+    if (items == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((items + 3) / 4);
+    if (bf16)
+        qk_norm_rope_kernel<__bf16><<<grid, 256, 0, st>>>(
+            (const __bf16*)qkv, T, H, g_q, g_k, cos_t, sin_t, eps, (__bf16*)q_out, (__bf16*)k_out,
+            ldk, (__bf16*)v_out, ldv);
+    else
+        qk_norm_rope_kernel<float><<<grid, 256, 0, st>>>(
+            (const float*)qkv, T, H, g_q, g_k, cos_t, sin_t, eps, (float*)q_out, (float*)k_out, ldk,
+            (float*)v_out, ldv);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- RoPE tables
+struct RopeSegs {
+    int32_t text_len;
+    int32_t n_img;
+    int32_t h[15], w[15];
+};
+
+__global__ void rope_tables_kernel(RopeSegs rs, int64_t row0, int64_t T_rows, double theta,
+                                   float* __restrict__ cos_out, float* __restrict__ sin_out) {
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T_rows * 64) return;
+    const int64_t r = idx / 64;
+    const int pair = (int)(idx % 64);
+    const int64_t p = row0 + r;
+    int64_t pf, ph, pw;
+    if (p < rs.text_len) {
+        pf = ph = pw = p;
+    } else {
+        int64_t off = p - rs.text_len;
+        int k = 0;
+        while (k < rs.n_img - 1 && off >= (int64_t)rs.h[k] * rs.w[k]) {
+            off -= (int64_t)rs.h[k] * rs.w[k];
+            ++k;
+        }
+        const int64_t y = off / rs.w[k], x = off % rs.w[k];
+        pf = rs.text_len + k;
+        ph = y - (rs.h[k] - rs.h[k] / 2);
+        pw = x - (rs.w[k] - rs.w[k] / 2);
+    }
+    int64_t pos;
+    int j, dim;
+    if (pair < 16) { pos = pf; j = pair; dim = 32; }
+    else if (pair < 40) { pos = ph; j = pair - 16; dim = 48; }
+    else { pos = pw; j = pair - 40; dim = 48; }
+    const double omega = pow(theta, -2.0 * (double)j / (double)dim);
+    const double phi = (double)pos * omega;
+    cos_out[idx] = (float)cos(phi);
+    sin_out[idx] = (float)sin(phi);
+}
+
+hipError_t launch_rope_tables(int32_t text_len, const int32_t* grids, int32_t n_img, int64_t row0,
+                              int64_t T_rows, float theta, float* cos_out, float* sin_out,
+                              hipStream_t st) {
+    RopeSegs rs{};
+    rs.text_len = text_len;
+    rs.n_img = n_img;
+    for (int k = 0; k < n_img; ++k) {
+        rs.h[k] = grids[2 * k];
+        rs.w[k] = grids[2 * k + 1];
+    }
+    const int64_t n = T_rows * 64;
+    if (n == 0) return hipSuccess;
+    rope_tables_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(rs, row0, T_rows, (double)theta,
+                                                                     cos_out, sin_out);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- dtype cast
+template <typename TI, typename TO>
+__global__ void cast_kernel(const TI* __restrict__ x, TO* __restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = from_f<TO>(to_f<TI>(x[i]));
+}
+
+hipError_t launch_cast(const void* x, bool x_bf16, void* y, bool y_bf16, int64_t n, hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (x_bf16 && y_bf16)
+        cast_kernel<__bf16, __bf16><<<grid, 256, 0, st>>>((const __bf16*)x, (__bf16*)y, n);
+    else if (x_bf16)
+        cast_kernel<__bf16, float><<<grid, 256, 0, st>>>((const __bf16*)x, (float*)y, n);
+    else if (y_bf16)
+        cast_kernel<float, __bf16><<<grid, 256, 0, st>>>((const float*)x, (__bf16*)y, n);
+    else
+        cast_kernel<float, float><<<grid, 256, 0, st>>>((const float*)x, (float*)y, n);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- Euler
+template <typename T>
+__global__ void euler_kernel(float* __restrict__ x, const T* __restrict__ v, int64_t n, float dt) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) x[i] = x[i] + dt * to_f<T>(v[i]);
+}
+
+hipError_t launch_euler(float* x, const void* v, bool bf16, int64_t n, float sigma, float sigma_next,
+                        hipStream_t st) {
+    if (n == 0) return hipSuccess;
+    const float dt = sigma_next - sigma;
+    const unsigned grid = (unsigned)((n + 255) / 256);
+    if (bf16)
+        euler_kernel<__bf16><<<grid, 256, 0, st>>>(x, (const __bf16*)v, n, dt);
+    else
+        euler_kernel<float><<<grid, 256, 0, st>>>(x, (const float*)v, n, dt);
+    return hipGetLastError();
+}
+
+}  // namespace dit

@@ -1,0 +1,74 @@
+// Internal launchers (host side) of the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "common.h"
+
+namespace dit {
+
+enum EpiKind : int32_t { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2 };
+
+// What the GEMM does with each output element v = acc (fp32 or bf16 GEMM) or
+// v = acc * a_scale[m] * w_scale[n] (int8 GEMM), after adding bias[n]:
+//   EPI_STORE: y[m, n] = v (bf16-rounded if y_bf16); acc_out[m, n] = int32 acc.
+//   EPI_GELU:  u = round(v); y[m, n] = round(GELU_tanh(u)).
+//   EPI_RESID: y = round(v); x[m, n] = round(x[m, n] + gate[set(m)][n] * y).
+// round() is bf16 rounding when act_bf16, identity in fp32 mode.
+struct EpiParams {
+    int32_t kind;
+    int32_t act_bf16;      // bf16 storage semantics for rounding and x
+    int32_t y_bf16;        // output dtype of EPI_STORE / EPI_GELU
+    const float* a_scale;  // int8 GEMM only
+    const float* w_scale;
+    const float* bias;     // may be NULL
+    void* y;
+    int64_t ldy;
+    int32_t* acc_out;      // may be NULL
+    int64_t ldacc;
+    void* x;               // EPI_RESID
+    int64_t ldx;
+    const float* gate;     // gate row of modulation set 0; set s at gate + s * gate_stride
+    int64_t gate_stride;
+    SegMap sm;
+};
+
+hipError_t launch_gemm_i8(const int8_t* a, const int8_t* w, int64_t M, int64_t N, int64_t K,
+                          const EpiParams& ep, hipStream_t st);
+hipError_t launch_gemm_bf16(const void* a, int64_t lda, const void* w, int64_t M, int64_t N,
+                            int64_t K, const EpiParams& ep, hipStream_t st);
+hipError_t launch_gemm_f32(const float* a, int64_t lda, const float* w, int64_t M, int64_t N,
+                           int64_t K, const EpiParams& ep, hipStream_t st);
+
+hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
+                                int8_t* q, float* scale, hipStream_t st);
+hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
+                        const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
+                        float* qs, hipStream_t st);
+hipError_t launch_adaln_small(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
+                              const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
+                              float* qs, hipStream_t st);
+hipError_t launch_qk_norm_rope(const void* qkv, bool bf16, int64_t T, int H, const float* g_q,
+                               const float* g_k, const float* cos_t, const float* sin_t, float eps,
+                               void* q_out, void* k_out, int64_t ldk, void* v_out, int64_t ldv,
+                               hipStream_t st);
+hipError_t launch_rope_tables(int32_t text_len, const int32_t* grids, int32_t n_img, int64_t row0,
+                              int64_t T_rows, float theta, float* cos_out, float* sin_out,
+                              hipStream_t st);
+hipError_t launch_cast(const void* x, bool x_bf16, void* y, bool y_bf16, int64_t n, hipStream_t st);
+hipError_t launch_euler(float* x, const void* v, bool bf16, int64_t n, float sigma, float sigma_next,
+                        hipStream_t st);
+
+// Attention: kv_end[s] = end position of segment s (keys [0, kv_end[seg]) are
+// visible to a query of segment seg).
+struct AttnSegs {
+    int64_t end[kMaxSeg];
+    int32_t n;
+};
+hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, int64_t T_q,
+                                 int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
+                                 int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st);
+hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, int64_t T_q,
+                                int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
+                                int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st);
+
+}  // namespace dit

@@ -1,0 +1,243 @@
+/*
+ * dit.h - C ABI of the MI355X (gfx950) single-stream DiT block library.
+ *
+ * The block is the one every denoise step of Qwen-Image-2.1 runs 32 times: a
+ * 4096-wide single-stream DiT block over a [text | reference | target] token
+ * sequence ("RGBA-Image-2.1 - Core AI port of Qwen-Image-2.1", intro and Graph
+ * contracts; "qwen-image-mnn", What runs where).
+ *
+ * Conventions shared by every entry point
+ *  - Device pointers are plain device addresses (hipMalloc'd or torch tensors);
+ *    "host" arguments are ordinary host memory.  The caller owns every buffer.
+ *  - Matrices are row-major.  Weights are [N, K] with K contiguous (one output
+ *    channel per row).  bf16 data is IEEE bfloat16 (uint16 storage).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *    work on it: no allocation, no synchronization, so they can be captured
+ *    into a HIP graph.
+ *  - Every argument is checked before the first HIP call; an invalid call
+ *    returns a DIT_E_* code and launches nothing ("Qwen_Image-2.1-MXFP4-Paiton",
+ *    Tested operating limits: unsupported settings are rejected before GPU
+ *    execution).  DIT_E_HIP reports a failed launch.  dit_last_error() gives a
+ *    thread-local description of the last failure.  Nothing throws or aborts.
+ *  - Results are deterministic: the same inputs give bitwise-equal outputs.
+ */
+#ifndef DIT_H
+#define DIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DIT_ABI_VERSION 1
+
+typedef enum {
+    DIT_OK = 0,
+    DIT_E_NULL = 1,         /* a required pointer is NULL */
+    DIT_E_SHAPE = 2,        /* inconsistent or out-of-range sizes */
+    DIT_E_DTYPE = 3,        /* dtype or mode not accepted here */
+    DIT_E_ALIGN = 4,        /* pointer or stride not 16-byte aligned */
+    DIT_E_UNSUPPORTED = 5,  /* valid, but outside the supported set */
+    DIT_E_WORKSPACE = 6,    /* workspace NULL or too small */
+    DIT_E_HIP = 7           /* a HIP launch failed */
+} dit_status_t;
+
+typedef enum { DIT_F32 = 0, DIT_BF16 = 1, DIT_I8 = 2, DIT_I32 = 3 } dit_dtype_t;
+
+typedef enum {
+    DIT_MODE_F32 = 0,   /* everything fp32 */
+    DIT_MODE_BF16 = 1,  /* bf16 tensors, fp32 statistics/accumulators/softmax */
+    DIT_MODE_W8A8 = 2   /* bf16 mode with the four linears W8A8 */
+} dit_mode_t;
+
+int dit_abi_version(void);
+const char* dit_status_string(int status);
+const char* dit_last_error(void);
+
+/*
+ * Symmetric per-row int8 quantization ("Qwen-Image-2.1 W8A8 - FlagOS for Mac",
+ * Quantization and validation: dynamic per-token activations, per-output-channel
+ * weights, fp32 scales, zero point 0).  For each row m of x [M, K] (row stride ldx
+ * elements, dtype DIT_BF16 or DIT_F32): s = amax/127 (fp32), q = clamp(rint(x/s),
+ * -127, 127) with IEEE fp32 division and ties to even; an all-zero row gives s = 0
+ * and q = 0.  q [M, K] int8 (row stride K), scale [M] fp32.
+ * Supported: 1 <= K <= 32768 (bf16) or 16384 (f32), K % 8 == 0, ldx % 8 == 0,
+ * 16-byte aligned x and q.
+ */
+int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
+                      int8_t* q, float* scale, void* stream);
+
+/*
+ * W8A8 linear ("Qwen-Image-2.1 W8A8 - FlagOS for Mac", Quantization and
+ * validation: int8 x int8 with int32 accumulation, fp32 scaling, bf16 output).
+ *   y[m, n] = float(sum_k a[m,k] * w[n,k]) * a_scale[m] * w_scale[n] + bias[n]
+ * a [M, K] int8 (row stride K), w [N, K] int8 (row stride K), a_scale [M],
+ * w_scale [N], bias [N] fp32 or NULL.  y [M, N] with row stride ldy, dtype
+ * DIT_BF16 (rounded to nearest even) or DIT_F32.  If acc_out is not NULL the
+ * exact int32 sums are also stored there ([M, N], row stride N).
+ * Supported: K % 128 == 0, N % 16 == 0, K <= 133144 (so K*127^2 < 2^31).
+ */
+int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
+                const int8_t* w, const float* w_scale, const float* bias, int64_t N,
+                void* y, int y_dtype, int64_t ldy, int32_t* acc_out, void* stream);
+
+/*
+ * bf16 linear for the non-quantized linears: y = a w^T + bias with fp32
+ * accumulation.  a [M, K] bf16 (row stride lda), w [N, K] bf16 (row stride K),
+ * bias [N] fp32 or NULL, y [M, N] bf16 or fp32 (row stride ldy).
+ * Supported: K % 64 == 0, N % 16 == 0, lda % 8 == 0.
+ */
+int bf16_linear(const void* a, int64_t M, int64_t K, int64_t lda, const void* w,
+                const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy, void* stream);
+
+/*
+ * fp32 linear (fp32 mode): y = a w^T + bias, fp32 throughout.  a [M, K] f32
+ * (row stride lda), w [N, K] f32, y [M, N] f32 (row stride ldy).
+ * Supported: K % 16 == 0, N % 16 == 0.
+ */
+int f32_linear(const float* a, int64_t M, int64_t K, int64_t lda, const float* w,
+               const float* bias, int64_t N, float* y, int64_t ldy, void* stream);
+
+/*
+ * Block-causal attention ("RGBA-Image-2.1 - Core AI port", intro; "qwen-image-mnn",
+ * What runs where).  Keys are split into n_seg consecutive segments of lengths
+ * seg_len[] (host array, sum = T_k).  Query row i sits at absolute position
+ * T_k - T_q + i (so the first T_k - T_q keys may come from a prefix cache) and may
+ * attend key j iff segment(j) <= segment(T_k - T_q + i): each segment sees itself
+ * and every earlier one.  Per head h:
+ *   o[i, h, :] = sum_j softmax_j(sm_scale * q[i,h,:].k[j,h,:]) v[j,h,:]
+ * q [T_q, H, d], k and v [T_k, H, d], o [T_q, H, d]; ldq/ldk/ldv/ldo are row
+ * strides in elements between consecutive tokens (>= H*d).  dtype DIT_BF16
+ * (fp32 softmax, bf16 P for the PV product, bf16 output) or DIT_F32.
+ * sm_scale <= 0 means 1/sqrt(d).  Supported: d == 128, 1 <= T_q <= T_k,
+ * 1 <= n_seg <= 16, strides % 8 == 0.
+ */
+int block_causal_attention(const void* q, const void* k, const void* v, void* o, int dtype,
+                           int64_t T_q, int64_t T_k, int32_t H, int32_t d, int64_t ldq,
+                           int64_t ldk, int64_t ldv, int64_t ldo, const int32_t* seg_len,
+                           int32_t n_seg, float sm_scale, void* stream);
+
+/*
+ * 3-axis RoPE tables ("RGBA-Image-2.1 - Core AI port", Graph contracts, RoPE).
+ * Sequence = [text (text_len tokens) | image 0 | image 1 | ...]; image k is a
+ * grids[2k] x grids[2k+1] (h x w) latent grid in raster order (host array).
+ * Positions: text token i -> (i, i, i); image k token (y, x) -> (text_len + k,
+ * y - (h - h/2), x - (w - w/2)) with integer halving.  Head-dim pairs 0..15 use
+ * the frame position, 16..39 the height, 40..63 the width; pair j of an axis
+ * with dim d_a (32, 48, 48) turns by pos * theta^(-2j/d_a).  Writes
+ * cos/sin [T_rows, 64] fp32 for sequence rows [row0, row0 + T_rows) (angles in
+ * fp64, rounded once to fp32).  Supported: n_img <= 15.
+ */
+int dit_rope_tables(int32_t text_len, const int32_t* grids, int32_t n_img, int64_t row0,
+                    int64_t T_rows, float theta, float* cos_out, float* sin_out, void* stream);
+
+/*
+ * Q/K RMSNorm + RoPE, the QKV epilogue of the block ("Qwen Image 2.1 native
+ * qualification", Numerical checks: the normalized value is cast to the gain's
+ * dtype before the gain multiply).  qkv [T, 3*H*128] (row stride 3*H*128) holds
+ * the linear output [q | k | v].  Per token and head:
+ *   n = t / sqrt(mean(t^2) + eps); bf16 mode: n -> bf16, n*g -> bf16; then the
+ *   interleaved pair rotation by cos/sin [T, 64]; bf16 mode rounds once more.
+ * Writes q_out [T, H*128], k_out and v_out (row strides ldk, ldv, e.g. rows of a
+ * K/V cache).  dtype DIT_BF16 or DIT_F32 for all tensors; g_q, g_k [128] fp32.
+ */
+int dit_qk_norm_rope(const void* qkv, int dtype, int64_t T, int32_t H, const float* g_q,
+                     const float* g_k, const float* cos_t, const float* sin_t, float eps,
+                     void* q_out, void* k_out, int64_t ldk, void* v_out, int64_t ldv,
+                     void* stream);
+
+/*
+ * adaLN prologue: h = LayerNorm(x) * (1 + scale) + shift (no affine, biased
+ * variance, fp32 statistics) with one (shift, scale) pair [D] fp32 for all rows.
+ * x [M, D] bf16 or f32 (row stride D).  Output either h [M, D] (h_dtype bf16 or
+ * f32; bf16 rounds once), or, when q_out is not NULL, the bf16-rounded h
+ * quantized per row as in dit_quantize_rows (q_out [M, D] int8, q_scale [M]).
+ * Supported: D % 256 == 0, D <= 8192.
+ */
+int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const float* shift,
+                       const float* scale, float eps, void* h_out, int h_dtype, int8_t* q_out,
+                       float* q_scale, void* stream);
+
+/* FlowMatch Euler update ("RGBA-Image-2.1 - Core AI port", Graph contracts,
+ * Sampler): x[i] += (sigma_next - sigma) * v[i] in fp32; x fp32, v bf16 or f32. */
+int dit_euler_step(float* x, const void* v, int v_dtype, int64_t n, float sigma,
+                   float sigma_next, void* stream);
+
+/* Element-wise dtype conversion (fp32 <-> bf16, round to nearest even), e.g. the
+ * fp32 sampler latent entering a bf16 DiT ("RGBA-Image-2.1 - Core AI port",
+ * Graph contracts: fp32 graph inputs and outputs around bf16 compute).
+ * x and y may not overlap. */
+int dit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* stream);
+
+/* ------------------------------------------------------------------ the block */
+
+typedef struct {
+    int32_t mode;       /* dit_mode_t */
+    int32_t D;          /* width; D == H * head_dim */
+    int32_t H;          /* heads */
+    int32_t head_dim;   /* must be 128 */
+    int32_t F;          /* MLP width */
+    float ln_eps;       /* adaLN LayerNorm eps (1e-6) */
+    float qk_eps;       /* Q/K RMSNorm eps (1e-6) */
+} dit_block_config;
+
+typedef struct {
+    /* [N, K] row-major: int8 codes (W8A8), bf16 (BF16) or f32 (F32).
+       w_qkv [3D, D] (q | k | v rows), w_o [D, D], w_1 [F, D], w_2 [D, F]. */
+    const void *w_qkv, *w_o, *w_1, *w_2;
+    /* per-output-channel fp32 scales (W8A8 only, else NULL) */
+    const float *s_qkv, *s_o, *s_1, *s_2;
+    /* fp32 biases [3D], [D], [F], [D] */
+    const float *b_qkv, *b_o, *b_1, *b_2;
+    /* Q/K RMSNorm gains [128] fp32, shared by all heads */
+    const float *g_q, *g_k;
+} dit_block_weights;
+
+typedef struct {
+    void* x;                    /* [T_q, D] in/out, bf16 (f32 in F32 mode) */
+    const float* mod;           /* [n_mod, 6, D]: shift1, scale1, gate1, shift2, scale2, gate2 */
+    int32_t n_mod;
+    const int32_t* mod_of_seg;  /* host [n_seg]: modulation set of each segment */
+    const float* cos_t;         /* [T_q, 64] RoPE tables of the computed rows */
+    const float* sin_t;
+    const int32_t* seg_len;     /* host [n_seg], sum = T_k */
+    int32_t n_seg;
+    int64_t T_q;                /* rows computed (the last T_q rows of the sequence) */
+    int64_t T_k;                /* sequence length */
+    void* k_cache;              /* [T_k, H, 128] K (post-norm, post-RoPE); rows [0, T_k-T_q) */
+    void* v_cache;              /*   are read, rows [T_k-T_q, T_k) are written by the call */
+} dit_block_io;
+
+/* Workspace the block needs for T_q computed rows (bytes, 256-aligned pieces). */
+size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k);
+
+/*
+ * One single-stream DiT block on the last T_q rows of a T_k-token sequence:
+ *   h  = LN(x)(1+scale1)+shift1;  [q|k|v] = h Wqkv^T + b_qkv
+ *   q, k <- RoPE(RMSNorm(q, k) * g);  K/V rows -> cache
+ *   o  = block-causal attention(q, K cache, V cache)
+ *   x1 = x + gate1 * (o Wo^T + b_o)
+ *   x  = x1 + gate2 * (GELU_tanh((LN(x1)(1+scale2)+shift2) W1^T + b1) W2^T + b2)
+ * Each row uses the modulation set of its segment.  In W8A8 mode the inputs of
+ * the four linears are quantized per token (dit_quantize_rows) and the weights
+ * are int8 codes with per-output-channel scales.  Supported: head_dim == 128,
+ * D == H*128, D % 256 == 0, F % 256 == 0, D <= 8192, 1 <= n_seg <= 16.
+ */
+int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w,
+                      const dit_block_io* io, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/* The same block applied n_blocks times in order (one denoise step's stack);
+ * weights[b] is block b.  io->x is updated in place; k_cache/v_cache (if not
+ * NULL) are arrays of n_blocks per-block caches. */
+int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weights,
+                      int32_t n_blocks, const dit_block_io* io, void* const* k_caches,
+                      void* const* v_caches, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DIT_H */

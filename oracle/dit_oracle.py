@@ -27,7 +27,7 @@ import numpy as np
 
 __all__ = [
     "round_bf16", "quantize_rows", "int8_matmul_exact", "w8a8_linear", "linear",
-    "adaln_modulate", "qk_rmsnorm", "apply_gain", "rope_positions", "rope_tables", "apply_rope",
+    "adaln_modulate", "qk_rmsnorm", "apply_gain", "block_forward_rows", "rope_positions", "rope_tables", "apply_rope",
     "segment_ids", "allowed_mask", "attention", "gelu_tanh", "block_forward",
     "quantize_block_weights", "dit_step", "euler_update", "rel_l2", "HEAD_DIM",
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
@@ -97,7 +97,14 @@ def int8_matmul_exact(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
     K = qa.shape[-1]
     assert qw.shape[-1] == K
     assert K * 127 * 127 < 2 ** 53
-    return np.rint(qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+    if K <= 1024:
+        return np.rint(qa.astype(np.float64) @ qw.astype(np.float64).T).astype(np.int64)
+    # Same exactness argument in fp32 for chunks of 1024: |partial sums| <= 1024*127^2 < 2^24.
+    acc = np.zeros((qa.shape[0], qw.shape[0]), dtype=np.int64)
+    for k0 in range(0, K, 1024):
+        part = qa[:, k0:k0 + 1024].astype(np.float32) @ qw[:, k0:k0 + 1024].astype(np.float32).T
+        acc += np.rint(part).astype(np.int64)
+    return acc
 
 
 def w8a8_linear(qa, sa, qw, sw, bias) -> np.ndarray:
@@ -323,6 +330,68 @@ def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
     x2 = _store(x1 + gate2 * y2, mode)
     return {"x_out": x2, "k": k, "v": v, "q": q, "h": h, "qkv": qkv, "o": o,
             "x1": x1, "h2": h2, "u": u, "g": g}
+
+
+def block_forward_rows(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str, rows,
+                       k_prefix=None, v_prefix=None, qweights=None,
+                       ln_eps: float = LN_EPS, qk_eps: float = QK_EPS) -> Dict[str, np.ndarray]:
+    """``block_forward`` restricted to the output rows ``rows`` (indices into x).
+
+    Keys and values are needed for every row, so the adaLN prologue and the QKV
+    linear run on all rows; every later step runs on the requested rows only.
+    Row-local steps give the same values as the full computation.
+    """
+    x = np.asarray(x, np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    T_q, D = x.shape
+    H = D // HEAD_DIM
+    if mode == "w8a8" and qweights is None:
+        qweights = quantize_block_weights(weights)
+    m = _row_mod(mod, mod_of_seg, seg_len, T_q)
+    shift1, scale1, gate1, shift2, scale2, gate2 = (m[:, i, :] for i in range(6))
+    h = _store(adaln_modulate(x, shift1, scale1, ln_eps), mode)
+    kv = _store(_lin_cols(h, weights, qweights, mode, D, 3 * D), mode)
+    k = _store(apply_rope(qk_rmsnorm(kv[:, :D].reshape(T_q, H, HEAD_DIM), weights["g_k"], mode, qk_eps),
+                          cos, sin), mode)
+    v = kv[:, D:].reshape(T_q, H, HEAD_DIM)
+    qr = _store(_lin_cols(h[rows], weights, qweights, mode, 0, D), mode).reshape(len(rows), H, HEAD_DIM)
+    qr = _store(apply_rope(qk_rmsnorm(qr, weights["g_q"], mode, qk_eps), cos[rows], sin[rows]), mode)
+    if k_prefix is not None and len(k_prefix):
+        k_all = np.concatenate([np.asarray(k_prefix, np.float64), k], axis=0)
+        v_all = np.concatenate([np.asarray(v_prefix, np.float64), v], axis=0)
+    else:
+        k_all, v_all = k, v
+    T_k = k_all.shape[0]
+    allowed = allowed_mask(seg_len, T_q)[rows]
+    scale = 1.0 / math.sqrt(HEAD_DIM)
+    o = np.empty((len(rows), H, HEAD_DIM))
+    for hd in range(H):
+        sc = (qr[:, hd, :] @ k_all[:, hd, :].T) * scale
+        sc = np.where(allowed, sc, -np.inf)
+        sc = sc - sc.max(axis=1, keepdims=True)
+        p = np.exp(sc)
+        o[:, hd, :] = (p / p.sum(axis=1, keepdims=True)) @ v_all[:, hd, :]
+    assert T_k == allowed.shape[1]
+    o = _store(o, mode).reshape(len(rows), D)
+    xr = x[rows]
+    y = _store(_lin(o, "w_o", weights, qweights, mode), mode)
+    x1 = _store(xr + gate1[rows] * y, mode)
+    h2 = _store(adaln_modulate(x1, shift2[rows], scale2[rows], ln_eps), mode)
+    u = _store(_lin(h2, "w_1", weights, qweights, mode), mode)
+    g = _store(gelu_tanh(u), mode)
+    y2 = _store(_lin(g, "w_2", weights, qweights, mode), mode)
+    x2 = _store(x1 + gate2[rows] * y2, mode)
+    return {"x_out": x2, "k": k, "v": v, "q": qr, "o": o}
+
+
+def _lin_cols(a, weights, qweights, mode, c0, c1):
+    """Columns [c0, c1) of the QKV linear."""
+    b = weights["b_qkv"][c0:c1]
+    if mode == "w8a8":
+        qa, sa = quantize_rows(a)
+        qw, sw = qweights["w_qkv"]
+        return w8a8_linear(qa, sa, qw[c0:c1], sw[c0:c1], b)
+    return linear(a, weights["w_qkv"][c0:c1], b)
 
 
 # ----------------------------------------------------------------------------- one denoise step

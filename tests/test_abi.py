@@ -1,0 +1,152 @@
+"""The C-ABI library loads, exports every symbol of include/dit.h, and rejects
+invalid calls before any HIP call (CPU only: no compute is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diffusion_transformer_text_qwen_amd as dq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "dit.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s+\**([a-z_0-9]+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = dq.lib()
+    names = _header_functions()
+    assert len(names) >= 15, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(dq.exported_symbols())
+    assert lib.dit_abi_version() == 1
+
+
+def test_status_strings():
+    lib = dq.lib()
+    for s in range(8):
+        assert lib.dit_status_string(s)
+    assert lib.dit_status_string(99) == b"unknown status"
+
+
+NULL = None
+S = None  # default stream; never used since every call below fails validation
+
+
+def _err(code):
+    return code, dq.lib().dit_last_error().decode()
+
+
+def test_quantize_rows_validation():
+    lib = dq.lib()
+    assert lib.dit_quantize_rows(NULL, 7, 4, 64, 64, NULL, NULL, S) == 3          # dtype
+    assert lib.dit_quantize_rows(NULL, dq.BF16, 4, 64, 32, NULL, NULL, S) == 2    # ldx < K
+    assert lib.dit_quantize_rows(NULL, dq.BF16, 4, 60, 64, NULL, NULL, S) == 5    # K % 8
+    assert lib.dit_quantize_rows(NULL, dq.BF16, 4, 65536, 65536, NULL, NULL, S) == 5
+    assert lib.dit_quantize_rows(NULL, dq.BF16, 4, 64, 64, NULL, NULL, S) == 1    # NULL
+    assert lib.dit_quantize_rows(16, dq.BF16, 4, 64, 64, 24, 32, S) == 4          # misaligned q
+    assert lib.dit_quantize_rows(NULL, dq.BF16, 0, 64, 64, NULL, NULL, S) == 0    # empty: no-op
+
+
+def test_linear_validation():
+    lib = dq.lib()
+    assert lib.w8a8_linear(16, 16, 4, 100, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 5     # K % 128
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 60, 16, dq.BF16, 64, NULL, S) == 5     # N % 16
+    assert lib.w8a8_linear(16, 16, 4, 133248, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 5  # int32 bound
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.I8, 64, NULL, S) == 3
+    assert lib.w8a8_linear(NULL, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 1
+    assert lib.w8a8_linear(17, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 4
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 32, NULL, S) == 2     # ldy < N
+    assert lib.w8a8_linear(NULL, NULL, 0, 128, NULL, NULL, NULL, 64, NULL, dq.BF16, 64, NULL, S) == 0
+    assert lib.bf16_linear(16, 4, 96, 96, 16, NULL, 64, 16, dq.BF16, 64, S) == 5
+    assert lib.bf16_linear(16, 4, 64, 60, 16, NULL, 64, 16, dq.BF16, 64, S) == 2
+    assert lib.f32_linear(16, 4, 20, 20, 16, NULL, 64, 16, 64, S) == 5
+
+
+def _attn(dtype=dq.BF16, T_q=8, T_k=8, H=2, d=128, ld=256, segs=(3, 5), ptr=16):
+    arr = (ctypes.c_int32 * len(segs))(*segs) if segs is not None else None
+    return dq.lib().block_causal_attention(ptr, ptr, ptr, ptr, dtype, T_q, T_k, H, d, ld, ld, ld, ld,
+                                           ctypes.cast(arr, ctypes.c_void_p) if arr is not None else None,
+                                           len(segs) if segs is not None else 1, 0.0, S)
+
+
+def test_attention_validation():
+    assert _attn(d=64) == 5
+    assert _attn(dtype=dq.I8) == 3
+    assert _attn(T_q=9) == 2                     # T_q > T_k
+    assert _attn(segs=(3, 4)) == 2               # sum != T_k
+    assert _attn(segs=None) == 1
+    assert _attn(segs=tuple([1] * 8) + (0,) * 9, T_k=8) == 5   # 17 segments
+    assert _attn(ld=200) == 2
+    assert _attn(ld=260) == 4
+    assert _attn(ptr=NULL) == 1
+    assert _attn(ptr=24) == 4
+    assert _attn(T_q=0, ptr=NULL) == 0           # empty query set: no-op
+
+
+def test_rope_and_misc_validation():
+    lib = dq.lib()
+    g = (ctypes.c_int32 * 2)(8, 8)
+    gp = ctypes.cast(g, ctypes.c_void_p)
+    assert lib.dit_rope_tables(16, gp, 1, 0, 81, 10000.0, 16, 16, S) == 2      # past the end
+    assert lib.dit_rope_tables(16, gp, 16, 0, 8, 10000.0, 16, 16, S) == 5
+    assert lib.dit_rope_tables(16, None, 1, 0, 8, 10000.0, 16, 16, S) == 1
+    assert lib.dit_rope_tables(16, gp, 1, 0, 8, 10000.0, NULL, NULL, S) == 1
+    assert lib.dit_qk_norm_rope(16, dq.BF16, 4, 2, 16, 16, 16, 16, 1e-6, 16, 16, 100, 16, 256, S) == 2
+    assert lib.dit_adaln_modulate(16, dq.BF16, 4, 300, 16, 16, 1e-6, 16, dq.BF16, NULL, NULL, S) == 5
+    assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 16, dq.F32, NULL, NULL, S) == 3
+    assert lib.dit_euler_step(NULL, NULL, dq.F32, 10, 1.0, 0.5, S) == 1
+
+
+def _block_args(mode=dq.MODE_W8A8, D=512, H=4, F=2048, segs=(16, 64), T_q=80, mos=(0, 0), n_mod=1):
+    cfg = dq.BlockConfig(mode, D, H, 128, F, 1e-6, 1e-6)
+    w = dq.BlockWeightsC(**{n: 256 for n, _ in dq.BlockWeightsC._fields_})
+    sarr = (ctypes.c_int32 * len(segs))(*segs)
+    marr = (ctypes.c_int32 * len(mos))(*mos)
+    io = dq.BlockIO(x=256, mod=256, n_mod=n_mod, mod_of_seg=ctypes.cast(marr, ctypes.c_void_p), cos_t=256,
+                    sin_t=256, seg_len=ctypes.cast(sarr, ctypes.c_void_p), n_seg=len(segs), T_q=T_q,
+                    T_k=sum(segs), k_cache=256, v_cache=256)
+    return cfg, w, io, (sarr, marr)
+
+
+def test_block_validation():
+    lib = dq.lib()
+    need = lib.dit_block_workspace_bytes(ctypes.byref(dq.BlockConfig(2, 4096, 32, 128, 16384, 1e-6, 1e-6)),
+                                         17664, 17664)
+    assert need > 17664 * (4096 * 6 + 16384 * 3)
+
+    def call(cfg, w, io, ws=256, wsb=1 << 40):
+        return lib.dit_block_forward(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(io), ws, wsb, S)
+
+    cfg, w, io, keep = _block_args()
+    cfg.head_dim = 64
+    assert call(cfg, w, io) == 5
+    cfg, w, io, keep = _block_args(D=640, H=4)
+    assert call(cfg, w, io) == 2                       # D != H*128
+    cfg, w, io, keep = _block_args(mode=7)
+    assert call(cfg, w, io) == 3
+    cfg, w, io, keep = _block_args(F=1000)
+    assert call(cfg, w, io) == 5
+    cfg, w, io, keep = _block_args(segs=(16, 60))
+    assert call(cfg, w, io) == 2                       # T_q > T_k
+    cfg, w, io, keep = _block_args(mos=(0, 1))
+    assert call(cfg, w, io) == 2                       # mod set out of range
+    cfg, w, io, keep = _block_args()
+    w.s_o = None
+    assert call(cfg, w, io) == 1                       # W8A8 without scales
+    cfg, w, io, keep = _block_args()
+    io.k_cache = None
+    assert call(cfg, w, io) == 1
+    cfg, w, io, keep = _block_args()
+    assert call(cfg, w, io, ws=256, wsb=1024) == 6     # workspace too small
+    cfg, w, io, keep = _block_args()
+    io.x = 264
+    assert call(cfg, w, io) == 4
+    cfg, w, io, keep = _block_args(T_q=0)
+    assert call(cfg, w, io, ws=None, wsb=0) == 0       # nothing to compute

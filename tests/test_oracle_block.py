@@ -191,3 +191,16 @@ def test_dit_step_shapes_and_zero_velocity_identity():
     st0["b_proj_out"] = np.zeros_like(st["b_proj_out"])
     r0 = oracle.dit_step(st0, blocks, inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, "bf16")
     assert np.array_equal(r0["latent_next"], st["latent"].astype(np.float64))
+
+
+def test_sampled_rows_equal_full_block():
+    for mode in ("f32", "w8a8"):
+        w, wt, inp = _tiny(mode, grids=((2, 2), (3, 3)))
+        pos = oracle.rope_positions(w.text, w.images)
+        c, s = oracle.rope_tables(pos)
+        full = oracle.block_forward(inp["x"], inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, wt, mode)
+        rows = [0, 2, 5, 9, 15]
+        part = oracle.block_forward_rows(inp["x"], inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, wt,
+                                         mode, rows)
+        assert np.allclose(part["x_out"], full["x_out"][rows], rtol=1e-12, atol=1e-12), mode
+        assert np.allclose(part["k"], full["k"], rtol=1e-13, atol=1e-13)
