@@ -1,0 +1,316 @@
+"""Throughput of the single-stream DiT block path on one MI355X.
+
+Default workload (timed step): one denoise step of the 1024x1024 generation,
+i.e. 32 W8A8 blocks over [256 text | 4096 image] tokens (D 4096, 32 heads x 128,
+MLP 16384) plus the DiT head (img_in, txt_in), tail (final adaLN, proj_out) and
+the FlowMatch Euler update of the 4096 x 64 latent.  Reported value: DiT-block
+tokens/s = 32 * 4352 block rows / step time.
+
+Also measured (reported under "edit_2048px"): one block of the 2048x2048 edit
+workload, [256 text | 1024 reference | 16384 target], uncached step (17,664
+rows) and the cached step that reuses the prefix K/V (16,384 rows).
+
+Inputs are seeded synthetic tensors (ditsynth); the path runs entirely in the
+HIP library through its C ABI.  Per-launch kernel times come from HIP events
+recorded by the library around each launch in the timed region.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-edit]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DiT-block tokens/s at 4096/16384 img tokens; int8 GEMM & attn % of MFMA peak"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published (5.0 POP/s)
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published (8 TB/s)
+GEMM_SITES = ("qkv_gemm", "out_gemm", "up_gemm", "down_gemm")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_ops(T, D, F):
+    """Algorithmic int8 ops of the four linears of one block: 2*T*(3D*D + D*D + F*D + D*F)."""
+    return {"qkv_gemm": 2 * T * 3 * D * D, "out_gemm": 2 * T * D * D, "up_gemm": 2 * T * F * D,
+            "down_gemm": 2 * T * D * F}
+
+
+def attn_pairs(seg_len, T_q):
+    """Allowed (query, key) pairs: a query of segment s sees keys [0, end(s))."""
+    ends, acc = [], 0
+    for n in seg_len:
+        acc += n
+        ends.append(acc)
+    T_k = acc
+    pairs, start = 0, 0
+    for n, e in zip(seg_len, ends):
+        lo = max(start, T_k - T_q)
+        if e > lo:
+            pairs += (e - lo) * e
+        start = e
+    return pairs
+
+
+def hbm_bytes(T, D, F):
+    """Algorithmic HBM bytes of the HBM-bound launches of one W8A8 block."""
+    return {
+        "adaln1": T * (2 * D + D + 4),          # bf16 x in, int8 codes + scale out
+        "adaln2": T * (2 * D + D + 4),
+        "qk_norm_rope": T * (3 * D * 2 + 3 * D * 2 + 64 * 8),   # qkv in; q, k, v out; cos/sin
+        "quant_o": T * (2 * D + D + 4),
+        "quant_g": T * (2 * F + F + 4),
+    }
+
+
+def site_report(prof, per_block_ops, n_blocks_timed, peak, unit):
+    out = {}
+    for site, ops in per_block_ops.items():
+        p = prof.get(site, {"ms": 0.0, "count": 0})
+        if p["count"] == 0 or p["ms"] <= 0:
+            continue
+        avg_ms = p["ms"] / p["count"]
+        rate = ops / (avg_ms * 1e-3) / 1e12 if unit != "GB/s" else ops / (avg_ms * 1e-3) / 1e9
+        out[site] = {"avg_us": round(avg_ms * 1e3, 2), "count": p["count"], unit: round(rate, 1),
+                     "frac_peak": round(rate / peak, 4)}
+    return out
+
+
+def run_stack(args, dq, torch, ditsynth):
+    w = ditsynth.workload(3)
+    D, H, F, T, L = w.D, w.H, w.F, w.T, w.text
+    N = w.seg_len[-1]
+    dev = "cuda"
+    t0 = time.time()
+    blocks = []
+    for b in range(w.n_blocks):
+        t = {}
+        for name, a in ditsynth.device_block_weights(w, b, dev):
+            if name.startswith("w_"):
+                q = torch.empty(a.shape, dtype=torch.int8, device=dev)
+                s = torch.empty(a.shape[0], dtype=torch.float32, device=dev)
+                dq.quantize_rows(a, q, s)
+                t[name] = q
+                t["s" + name[1:]] = s
+            else:
+                t[name] = a
+            del a
+        blocks.append(dq.BlockWeights.from_device(t, "w8a8"))
+    si = ditsynth.device_step_inputs(w, dev)
+    torch.cuda.synchronize()
+    log(f"stack weights + inputs ready in {time.time() - t0:.1f}s")
+    cfg = dq.block_config("w8a8", D, H, F)
+    cos = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    sin = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    dq.rope_tables(L, w.images, 0, T, cos, sin)
+    kc = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(w.n_blocks)]
+    vc = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(w.n_blocks)]
+    ws = torch.empty(dq.workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
+    x = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
+    lat = si["latent"].clone()
+    lat_b = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
+    txt_b = si["txt_feats"].to(torch.bfloat16)
+    w_txt = si["w_txt_in"].to(torch.bfloat16)
+    w_img = si["w_img_in"].to(torch.bfloat16)
+    w_out = si["w_proj_out"].to(torch.bfloat16)
+    mod = si["mod"][0:1].contiguous()
+    mf = si["mod_final"][0]
+    hf = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
+    vel = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
+    mos = [0] * len(w.seg_len)
+    sigma, sigma_next = 1.0, 1.0 - 0.98 / 39.0
+
+    def step():
+        dq.cast(lat, lat_b)
+        dq.bf16_linear(txt_b, w_txt, si["b_txt_in"], x[:L])
+        dq.bf16_linear(lat_b, w_img, si["b_img_in"], x[L:])
+        dq.stack_forward(cfg, blocks, x, mod, mos, cos, sin, w.seg_len, kc, vc, ws)
+        dq.adaln_modulate(x[L:], mf[0], mf[1], h_out=hf)
+        dq.bf16_linear(hf, w_out, si["b_proj_out"], vel)
+        dq.euler_step(lat, vel, sigma, sigma_next)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ok = bool(torch.isfinite(x.float()).all().item()) and bool(torch.isfinite(lat).all().item())
+    dq.profile_begin(args.steps * w.n_blocks * 10 + 16)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    prof = dq.profile_end()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    return w, ms, prof, ok
+
+
+def run_edit(args, dq, torch, ditsynth, reps):
+    """One block of the 2048^2 edit workload: uncached step 1, cached step 2."""
+    w = ditsynth.workload(4)
+    D, H, F, T, L = w.D, w.H, w.F, w.T, w.text
+    P = w.prefix_len
+    dev = "cuda"
+    t = {}
+    for name, a in ditsynth.device_block_weights(w, 0, dev):
+        if name.startswith("w_"):
+            q = torch.empty(a.shape, dtype=torch.int8, device=dev)
+            s = torch.empty(a.shape[0], dtype=torch.float32, device=dev)
+            dq.quantize_rows(a, q, s)
+            t[name], t["s" + name[1:]] = q, s
+        else:
+            t[name] = a
+    bw = dq.BlockWeights.from_device(t, "w8a8")
+    si = ditsynth.device_step_inputs(w, dev)
+    cfg = dq.block_config("w8a8", D, H, F)
+    cos = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    sin = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    dq.rope_tables(L, w.images, 0, T, cos, sin)
+    kc = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    ws = torch.empty(dq.workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
+    mod = si["mod"]
+    x1 = torch.cat([si["x_prefix"], si["x_target"][0]]).to(torch.bfloat16)
+    x2 = si["x_target"][1].to(torch.bfloat16)
+    xa = torch.empty_like(x1)
+    xb = torch.empty_like(x2)
+    mos1 = [0, 0, 1]
+    mos2 = [0, 0, 2]
+    res = {}
+    for label, src, dst, mos, r0 in (("uncached", x1, xa, mos1, 0), ("cached", x2, xb, mos2, P)):
+        def call():
+            dst.copy_(src)
+            dq.block_forward(cfg, bw, dst, mod, mos, cos[r0:], sin[r0:], w.seg_len, kc, vc, ws)
+        call()
+        torch.cuda.synchronize()
+        dq.profile_begin(reps * 10 + 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        prof = dq.profile_end()
+        T_q = T - r0
+        blk_ms = sum(p["ms"] for p in prof.values()) / reps
+        att = prof["attention"]
+        att_flops = 4 * D * attn_pairs(w.seg_len, T_q)
+        att_tf = att_flops / (att["ms"] / att["count"] * 1e-3) / 1e12
+        gops = sum(gemm_ops(T_q, D, F).values())
+        gms = sum(prof[s]["ms"] for s in GEMM_SITES) / reps
+        res[label] = {
+            "rows": T_q, "block_ms": round(blk_ms, 3),
+            "block_tokens_per_s": round(T_q / (blk_ms * 1e-3), 1),
+            "wall_ms_incl_copy": round(e0.elapsed_time(e1) / reps, 3),
+            "attention_tflops": round(att_tf, 1), "attention_frac_bf16_peak": round(att_tf / PEAK_BF16_TFLOPS, 4),
+            "int8_gemm_tops": round(gops / (gms * 1e-3) / 1e12, 1),
+            "int8_gemm_frac_peak": round(gops / (gms * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+        }
+    return res
+
+
+def cpu_baseline(ditsynth):
+    """The oracle, untuned, on one block of the 32-block stack (all 4352 rows) on the host."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count()
+    w = ditsynth.workload(3)
+    wt = ditsynth.block_weights(w, 0)
+    inp = ditsynth.block_inputs(w)
+    c, s = oracle.rope_tables(oracle.rope_positions(w.text, w.images))
+    t0 = time.perf_counter()
+    out = oracle.block_forward(inp["x"], inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, wt, "w8a8")
+    dt = time.perf_counter() - t0
+    assert np.all(np.isfinite(out["x_out"]))
+    return {"value": round(w.T / dt, 1), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one W8A8 block (block 0 of 32) over all {w.T} rows of the 1024px workload, "
+                      f"fp64 NumPy oracle incl. its weight quantization; {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-edit", action="store_true")
+    ap.add_argument("--edit-reps", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              f"(the multi-GPU design is described, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ditsynth
+    import diffusion_transformer_text_qwen_amd as dq
+
+    dq.lib()
+    torch.cuda.set_device(0)
+    w, ms, prof, ok = run_stack(args, dq, torch, ditsynth)
+    T, D, F = w.T, w.D, w.F
+    n_timed = args.steps * w.n_blocks
+    value = w.n_blocks * T / (ms * 1e-3)
+    g_ops = gemm_ops(T, D, F)
+    gemm_ms = sum(prof[s]["ms"] for s in GEMM_SITES)
+    gemm_cnt = sum(prof[s]["count"] for s in GEMM_SITES)
+    total_ops = sum(g_ops.values()) * n_timed
+    avg_launch_ops = total_ops / gemm_cnt
+    avg_launch_s = gemm_ms * 1e-3 / gemm_cnt
+    achieved = avg_launch_ops / avg_launch_s / 1e12
+    att_flops = 4 * D * attn_pairs(w.seg_len, T)
+    kernels = {}
+    kernels.update(site_report(prof, g_ops, n_timed, PEAK_INT8_TOPS, "TOPS"))
+    kernels.update(site_report(prof, {"attention": att_flops}, n_timed, PEAK_BF16_TFLOPS, "TFLOPS"))
+    kernels.update(site_report(prof, hbm_bytes(T, D, F), n_timed, PEAK_HBM_GBS, "GB/s"))
+    block_ms = sum(p["ms"] for p in prof.values()) / n_timed
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8/bf16",
+        "data": "synthetic",
+        "config": {"workload": "stack_w8a8_1024px: one denoise step = DiT head + 32 W8A8 blocks over "
+                               "[256 text | 64x64 image] tokens + tail + Euler on the 4096x64 latent",
+                   "blocks": w.n_blocks, "tokens": T, "image_tokens": w.seg_len[-1], "hidden": D,
+                   "heads": w.H, "mlp": F, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": None,
+                     "kernel": "gemm_mfma_kernel<int8> (W8A8 linears, 4 launches per block)",
+                     "algorithmic_ops_per_launch": int(avg_launch_ops),
+                     "avg_launch_us": round(avg_launch_s * 1e6, 2)},
+        "kernels": kernels,
+        "block_ms_sum_of_launches": round(block_ms, 4),
+        "finite": ok,
+    }
+    if not args.no_edit:
+        line["edit_2048px"] = run_edit(args, dq, torch, ditsynth, args.edit_reps)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on one block ...")
+        line["cpu_baseline"] = cpu_baseline(ditsynth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,6 +67,9 @@ _SIGS = {
                             _vp], ctypes.c_int),
     "dit_euler_step": ([_vp, _vp, ctypes.c_int, _c_i64, _fp, _fp, _vp], ctypes.c_int),
     "dit_cast": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _c_i64, _vp], ctypes.c_int),
+    "dit_profile_begin": ([_c_i32], ctypes.c_int),
+    "dit_profile_end": ([_vp, _vp, _c_i32], ctypes.c_int),
+    "dit_site_name": ([_c_i32], ctypes.c_char_p),
     "dit_block_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64], ctypes.c_size_t),
     "dit_block_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), ctypes.POINTER(BlockIO),
                            _vp, ctypes.c_size_t, _vp], ctypes.c_int),
@@ -191,6 +194,21 @@ def euler_step(x, v, sigma: float, sigma_next: float, stream=None) -> None:
 
 def cast(x, y, stream=None) -> None:
     _check(lib().dit_cast(_p(x), _dt(x), _p(y), _dt(y), x.numel(), _stream(stream)), "dit_cast")
+
+
+N_SITES = 10
+
+
+def profile_begin(capacity: int) -> None:
+    _check(lib().dit_profile_begin(capacity), "dit_profile_begin")
+
+
+def profile_end() -> Dict[str, Dict[str, float]]:
+    """{site name: {"ms": summed ms, "count": launches}} of the launches recorded since begin."""
+    ms = (ctypes.c_double * N_SITES)()
+    cnt = (ctypes.c_int64 * N_SITES)()
+    _check(lib().dit_profile_end(ctypes.cast(ms, _vp), ctypes.cast(cnt, _vp), N_SITES), "dit_profile_end")
+    return {lib().dit_site_name(i).decode(): {"ms": ms[i], "count": cnt[i]} for i in range(N_SITES)}
 
 
 # ---------------------------------------------------------------- the block

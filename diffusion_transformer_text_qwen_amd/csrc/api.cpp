@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "../../include/dit.h"
 #include "kernels.h"
@@ -81,6 +82,29 @@ SegMap make_segmap(const int32_t* seg_len, const int32_t* mod_of_seg, int32_t n_
     m.row_offset = row_offset;
     return m;
 }
+
+// ---- launch timing (measurement only)
+struct Profiler {
+    bool on = false;
+    int cap = 0, used = 0;
+    std::vector<hipEvent_t> ev;
+    std::vector<int> site;
+} g_prof;
+
+struct ProfScope {
+    int idx = -1;
+    hipStream_t st;
+    ProfScope(int site, hipStream_t s) : st(s) {
+        if (g_prof.on && g_prof.used < g_prof.cap) {
+            idx = g_prof.used++;
+            g_prof.site[idx] = site;
+            (void)hipEventRecord(g_prof.ev[2 * idx], st);
+        }
+    }
+    ~ProfScope() {
+        if (idx >= 0) (void)hipEventRecord(g_prof.ev[2 * idx + 1], st);
+    }
+};
 
 EpiParams store_epi(void* y, int64_t ldy, bool y_bf16, const float* bias) {
     EpiParams ep{};
@@ -408,19 +432,28 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     };
 
     // S1: adaLN prologue 1 (fused per-token quantization in W8A8 mode)
+    {
+    ProfScope ps(DIT_SITE_ADALN1, st);
     RUN(launch_adaln(x, bf, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
         "adaln1");
+    }
     // S2: QKV linear -> qkv (bf16-rounded in bf16 modes)
     {
         EpiParams ep = store_epi(qkv, 3 * D, bf, w->b_qkv);
+        ProfScope ps(DIT_SITE_QKV_GEMM, st);
         RUN(gemm(h, a8, sa, w->w_qkv, w->s_qkv, 3 * D, D, ep), "qkv_gemm");
     }
     // S3: Q/K RMSNorm + RoPE, K/V rows into the cache
+    {
+    ProfScope ps(DIT_SITE_QK_NORM_ROPE, st);
     RUN(launch_qk_norm_rope(qkv, bf, T, H, w->g_q, w->g_k, io->cos_t, io->sin_t, cfg->qk_eps, qb, kc, D, vc,
                             D, st),
         "qk_norm_rope");
+    }
     // S4: block-causal attention over the whole cache
     const float scale = 1.0f / std::sqrt(128.0f);
+    {
+    ProfScope ps(DIT_SITE_ATTENTION, st);
     if (bf)
         RUN(launch_attention_bf16(qb, k_cache, v_cache, ob, T, io->T_k, H, D, D, D, D, segs, scale, st),
             "attention");
@@ -428,8 +461,12 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
         RUN(launch_attention_f32((const float*)qb, (const float*)k_cache, (const float*)v_cache, (float*)ob, T,
                                  io->T_k, H, D, D, D, D, segs, scale, st),
             "attention");
+    }
     // S5 + S6: quantize o, out-projection with gated residual into x
-    if (q8) RUN(launch_quantize_rows(ob, true, T, D, D, o8, so, st), "quantize_o");
+    if (q8) {
+        ProfScope ps(DIT_SITE_QUANT_O, st);
+        RUN(launch_quantize_rows(ob, true, T, D, D, o8, so, st), "quantize_o");
+    }
     {
         EpiParams ep{};
         ep.kind = EPI_RESID;
@@ -440,11 +477,15 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
         ep.gate = io->mod + 2 * D;
         ep.gate_stride = mstride;
         ep.sm = sm;
+        ProfScope ps(DIT_SITE_OUT_GEMM, st);
         RUN(gemm(ob, o8, so, w->w_o, w->s_o, D, D, ep), "out_gemm");
     }
     // S7: adaLN prologue 2
+    {
+    ProfScope ps(DIT_SITE_ADALN2, st);
     RUN(launch_adaln(x, bf, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
         "adaln2");
+    }
     // S8: MLP up + GELU
     {
         EpiParams ep{};
@@ -454,10 +495,14 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
         ep.bias = w->b_1;
         ep.y = gb;
         ep.ldy = F;
+        ProfScope ps(DIT_SITE_UP_GEMM, st);
         RUN(gemm(h, a8, sa, w->w_1, w->s_1, F, D, ep), "up_gemm");
     }
     // S9 + S10: quantize g, MLP down with gated residual into x
-    if (q8) RUN(launch_quantize_rows(gb, true, T, F, F, g8, sg, st), "quantize_g");
+    if (q8) {
+        ProfScope ps(DIT_SITE_QUANT_G, st);
+        RUN(launch_quantize_rows(gb, true, T, F, F, g8, sg, st), "quantize_g");
+    }
     {
         EpiParams ep{};
         ep.kind = EPI_RESID;
@@ -468,6 +513,7 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
         ep.gate = io->mod + 5 * D;
         ep.gate_stride = mstride;
         ep.sm = sm;
+        ProfScope ps(DIT_SITE_DOWN_GEMM, st);
         RUN(gemm(gb, g8, sg, w->w_2, w->s_2, D, F, ep), "down_gemm");
     }
     return DIT_OK;
@@ -523,6 +569,62 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
         if (s) return s;
     }
     return DIT_OK;
+}
+
+int dit_profile_begin(int32_t capacity) {
+    CHECK(!g_prof.on, DIT_E_UNSUPPORTED, "profiling already active");
+    CHECK(capacity >= 1 && capacity <= (1 << 20), DIT_E_SHAPE, "capacity outside [1, 2^20]");
+    g_prof.ev.assign(2 * (size_t)capacity, nullptr);
+    g_prof.site.assign((size_t)capacity, 0);
+    for (auto& e : g_prof.ev) {
+        hipError_t r = hipEventCreate(&e);
+        if (r != hipSuccess) {
+            for (auto& f : g_prof.ev)
+                if (f) (void)hipEventDestroy(f);
+            g_prof.ev.clear();
+            return hip_status(r, "hipEventCreate");
+        }
+    }
+    g_prof.cap = capacity;
+    g_prof.used = 0;
+    g_prof.on = true;
+    return DIT_OK;
+}
+
+int dit_profile_end(double* ms_out, int64_t* count_out, int32_t n_sites) {
+    CHECK(g_prof.on, DIT_E_UNSUPPORTED, "profiling not active");
+    CHECK(ms_out && count_out, DIT_E_NULL, "ms_out and count_out must be non-NULL");
+    CHECK(n_sites >= 1, DIT_E_SHAPE, "n_sites must be >= 1");
+    for (int i = 0; i < n_sites; ++i) {
+        ms_out[i] = 0.0;
+        count_out[i] = 0;
+    }
+    int status = DIT_OK;
+    for (int i = 0; i < g_prof.used; ++i) {
+        float ms = 0.0f;
+        hipError_t r = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (r != hipSuccess) {
+            status = hip_status(r, "hipEventElapsedTime");
+            break;
+        }
+        const int s = g_prof.site[i];
+        if (s < n_sites) {
+            ms_out[s] += ms;
+            count_out[s] += 1;
+        }
+    }
+    for (auto& e : g_prof.ev) (void)hipEventDestroy(e);
+    g_prof.ev.clear();
+    g_prof.on = false;
+    g_prof.used = g_prof.cap = 0;
+    return status;
+}
+
+const char* dit_site_name(int32_t site) {
+    static const char* names[DIT_N_SITES] = {"adaln1", "qkv_gemm", "qk_norm_rope", "attention", "quant_o",
+                                             "out_gemm", "adaln2", "up_gemm", "quant_g", "down_gemm"};
+    return (site >= 0 && site < DIT_N_SITES) ? names[site] : "unknown";
 }
 
 }  // extern "C"

@@ -244,3 +244,72 @@ def rows(M: int, K: int, seed: int, scale: float = 1.0, bf16: bool = True, zero_
     for r in zero_rows:
         a[r] = 0.0
     return to_bf16_grid(a) if bf16 else a
+
+
+# --------------------------------------------------------------------------- device-side draws
+# The same distributions drawn with torch's device generator, for workloads too
+# large to draw on the host (the 32-block stack).  Different random numbers
+# than the host draws, same recipe.
+
+def _torch():
+    import torch
+    return torch
+
+
+def device_normal(shape, std, gen, device="cuda", bf16_grid=False):
+    torch = _torch()
+    t = torch.randn(shape, generator=gen, device=device, dtype=torch.float32) * std
+    if bf16_grid:
+        t = t.to(torch.bfloat16).to(torch.float32)
+    return t
+
+
+def device_generator(w: Workload, stream: int, device="cuda"):
+    torch = _torch()
+    g = torch.Generator(device=device)
+    g.manual_seed(int(np.random.SeedSequence([w.seed, stream]).generate_state(1)[0]))
+    return g
+
+
+def device_block_weights(w: Workload, block: int, device="cuda"):
+    """Yields (name, fp32 device tensor) for one block, masters first (see block_weights)."""
+    g = device_generator(w, 1000 + block, device)
+    D, F = w.D, w.F
+    for name, shape in (("w_qkv", (3 * D, D)), ("b_qkv", (3 * D,)), ("g_q", (HEAD_DIM,)),
+                        ("g_k", (HEAD_DIM,)), ("w_o", (D, D)), ("b_o", (D,)),
+                        ("w_1", (F, D)), ("b_1", (F,)), ("w_2", (D, F)), ("b_2", (D,))):
+        is_w = name.startswith("w_")
+        t = device_normal(shape, 0.02, g, device, bf16_grid=(w.mode == "bf16" or not is_w))
+        if name.startswith("g_"):
+            t = (t + 1.0).to(_torch().bfloat16).to(_torch().float32)
+        yield name, t
+
+
+def device_step_inputs(w: Workload, device="cuda"):
+    """Device versions of block_inputs (step 0) and step_inputs."""
+    torch = _torch()
+    g = device_generator(w, 1, device)
+    D, L, N = w.D, w.text, w.seg_len[-1]
+    out = {
+        "latent": device_normal((N, 64), 1.0, g, device),
+        "txt_feats": device_normal((L, D), 1.0, g, device, True),
+        "w_img_in": device_normal((D, 64), 0.02, g, device, True),
+        "b_img_in": device_normal((D,), 0.02, g, device, True),
+        "w_txt_in": device_normal((D, D), 0.02, g, device, True),
+        "b_txt_in": device_normal((D,), 0.02, g, device, True),
+        "w_proj_out": device_normal((64, D), 0.02, g, device, True),
+        "b_proj_out": device_normal((64,), 0.02, g, device, True),
+    }
+    for name, rows, n_sets in (("mod", 6, 1 + (w.steps if w.steps > 1 else 0)), ("mod_final", 2, 1)):
+        w_mod = device_normal((rows * D, D), 0.02, g, device)
+        b_mod = device_normal((rows * D,), 0.02, g, device)
+        sets = []
+        for _ in range(max(n_sets, 1)):
+            temb = device_normal((D,), 1.0, g, device)
+            silu = temb / (1.0 + torch.exp(-temb))
+            sets.append((w_mod @ silu + b_mod).reshape(rows, D))
+        out[name] = torch.stack(sets).contiguous()
+        del w_mod
+    out["x_target"] = [device_normal((N, D), 1.0, g, device, True) for _ in range(w.steps)]
+    out["x_prefix"] = device_normal((w.prefix_len, D), 1.0, g, device, True)
+    return out

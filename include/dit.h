@@ -237,6 +237,29 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
                       void* const* v_caches, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* ------------------------------------------------------------------ tracing */
+
+/* Launch sites of the block, in launch order. */
+typedef enum {
+    DIT_SITE_ADALN1 = 0, DIT_SITE_QKV_GEMM, DIT_SITE_QK_NORM_ROPE, DIT_SITE_ATTENTION,
+    DIT_SITE_QUANT_O, DIT_SITE_OUT_GEMM, DIT_SITE_ADALN2, DIT_SITE_UP_GEMM, DIT_SITE_QUANT_G,
+    DIT_SITE_DOWN_GEMM, DIT_N_SITES
+} dit_site_t;
+
+/*
+ * Per-launch kernel timing with HIP events (measurement only).  dit_profile_begin
+ * creates `capacity` event pairs (this allocates; call it outside any timed or
+ * captured region); while active, every kernel that dit_block_forward or
+ * dit_stack_forward launches records a start and an end event on its stream
+ * (at most `capacity` launches are recorded; later ones are counted in nothing).
+ * dit_profile_end waits for the recorded events, writes per site the summed
+ * milliseconds (ms_out[n_sites]) and launch counts (count_out[n_sites]), frees
+ * the events and stops recording.  Not for use from several threads at once.
+ */
+int dit_profile_begin(int32_t capacity);
+int dit_profile_end(double* ms_out, int64_t* count_out, int32_t n_sites);
+const char* dit_site_name(int32_t site);
+
 #ifdef __cplusplus
 }
 #endif
