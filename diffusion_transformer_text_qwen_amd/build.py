@@ -14,6 +14,9 @@ SOURCES = ["api.cpp", "elementwise.hip", "gemm.hip", "attention.hip"]
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the AGPR form makes the compiler rotate
+    # accumulators through copies inside the K loop.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-pragmas",
 ]
 

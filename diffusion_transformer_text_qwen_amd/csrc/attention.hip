@@ -24,12 +24,14 @@ constexpr int AK = 64;                  // keys per tile
 constexpr int KS_STRIDE = 128 * 2 + 16; // bytes per key row of the K tile
 constexpr int VT_STRIDE = AK * 2 + 8;   // bytes per d row of the transposed V tile
 
+// Keys visible to a query at absolute position pos: [0, end of its segment).
+// Static indices only (keeps the argument struct out of private memory).
 __device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
-    int s = 0;
-#pragma unroll 1
-    for (; s < sg.n - 1; ++s)
-        if (pos < sg.end[s]) break;
-    return sg.end[s];
+    int64_t e = sg.end[0];
+#pragma unroll
+    for (int s = 0; s < kMaxSeg - 1; ++s)
+        if (s < sg.n - 1 && pos >= sg.end[s]) e = sg.end[s + 1];
+    return e;
 }
 
 __global__ void __launch_bounds__(256, 2)

@@ -67,13 +67,15 @@ struct SegMap {
     int64_t row_offset;
 };
 
+// Unrolled with static indices only, so the argument struct stays in
+// registers / the kernel-argument segment (no private copy).
 __device__ __forceinline__ int seg_set(const SegMap& sm, int64_t row) {
     const int64_t p = sm.row_offset + row;
-    int s = 0;
-#pragma unroll 1
-    for (; s < sm.n - 1; ++s)
-        if (p < sm.end[s]) break;
-    return sm.set[s];
+    int set = sm.set[0];
+#pragma unroll
+    for (int s = 0; s < kMaxSeg - 1; ++s)
+        if (s < sm.n - 1 && p >= sm.end[s]) set = sm.set[s + 1];
+    return set;
 }
 
 // Symmetric int8 code of v for scale s (s == 0 -> 0); IEEE fp32 division,

@@ -15,18 +15,22 @@ __device__ __forceinline__ float gelu_tanh(float u) {
     return 0.5f * u * (1.0f + tanhf(k0 * (u + 0.044715f * u * u * u)));
 }
 
+// Epilogue variants, fixed per kernel instantiation (keeps one path live).
+enum EpiVariant : int { EV_STORE = 0, EV_STORE_ACC = 1, EV_GELU = 2, EV_RESID = 3 };
+
 // Apply the epilogue to one output element; v already holds acc*scales (+bias added here).
+template <int EV>
 __device__ __forceinline__ void epilogue(const EpiParams& ep, int64_t m, int64_t n, float v,
                                          int32_t acc_i) {
     if (ep.bias) v += ep.bias[n];
     const bool rb = ep.act_bf16 != 0;
-    if (ep.kind == EPI_STORE) {
+    if constexpr (EV == EV_STORE || EV == EV_STORE_ACC) {
         if (ep.y_bf16)
             reinterpret_cast<__bf16*>(ep.y)[m * ep.ldy + n] = to_bf16(v);
         else
             reinterpret_cast<float*>(ep.y)[m * ep.ldy + n] = v;
-        if (ep.acc_out) ep.acc_out[m * ep.ldacc + n] = acc_i;
-    } else if (ep.kind == EPI_GELU) {
+        if constexpr (EV == EV_STORE_ACC) ep.acc_out[m * ep.ldacc + n] = acc_i;
+    } else if constexpr (EV == EV_GELU) {
         const float u = rb ? bf16r(v) : v;
         const float g = gelu_tanh(u);
         if (ep.y_bf16)
@@ -47,12 +51,84 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, int64_t m, int64_t
     }
 }
 
+// Epilogue over 16 consecutive columns n0..n0+15 of row m (n0 % 16 == 0,
+// 16-byte aligned rows).  v[] holds acc * scales (int8 GEMM) or the fp32 sums.
+template <int EV>
+__device__ __forceinline__ void epilogue16(const EpiParams& ep, int64_t m, int64_t n0, float (&v)[16],
+                                           const int32_t (&acc)[16]) {
+    if (ep.bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + n0 + 4 * q);
+            v[4 * q] += b.x; v[4 * q + 1] += b.y; v[4 * q + 2] += b.z; v[4 * q + 3] += b.w;
+        }
+    }
+    const bool rb = ep.act_bf16 != 0;
+    if constexpr (EV != EV_RESID) {
+        if constexpr (EV == EV_GELU) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) v[e] = gelu_tanh(rb ? bf16r(v[e]) : v[e]);
+        }
+        if (ep.y_bf16) {
+            v8bf o0, o1;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                o0[e] = to_bf16(v[e]);
+                o1[e] = to_bf16(v[8 + e]);
+            }
+            v8bf* yp = reinterpret_cast<v8bf*>(reinterpret_cast<__bf16*>(ep.y) + m * ep.ldy + n0);
+            yp[0] = o0;
+            yp[1] = o1;
+        } else {
+            float4* yp = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.y) + m * ep.ldy + n0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yp[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+        if constexpr (EV == EV_STORE_ACC) {
+            int4* ap = reinterpret_cast<int4*>(ep.acc_out + m * ep.ldacc + n0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ap[q] = make_int4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+        }
+    } else {
+        const int set = seg_set(ep.sm, m);
+        const float* gate = ep.gate + (int64_t)set * ep.gate_stride + n0;
+        float gv[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 gq = *reinterpret_cast<const float4*>(gate + 4 * q);
+            gv[4 * q] = gq.x; gv[4 * q + 1] = gq.y; gv[4 * q + 2] = gq.z; gv[4 * q + 3] = gq.w;
+        }
+        if (rb) {
+            v8bf* xp = reinterpret_cast<v8bf*>(reinterpret_cast<__bf16*>(ep.x) + m * ep.ldx + n0);
+            v8bf x0 = xp[0], x1 = xp[1];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                x0[e] = to_bf16((float)x0[e] + gv[e] * bf16r(v[e]));
+                x1[e] = to_bf16((float)x1[e] + gv[8 + e] * bf16r(v[8 + e]));
+            }
+            xp[0] = x0;
+            xp[1] = x1;
+        } else {
+            float4* xp = reinterpret_cast<float4*>(reinterpret_cast<float*>(ep.x) + m * ep.ldx + n0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float4 xv = xp[q];
+                xv.x += gv[4 * q] * v[4 * q];
+                xv.y += gv[4 * q + 1] * v[4 * q + 1];
+                xv.z += gv[4 * q + 2] * v[4 * q + 2];
+                xv.w += gv[4 * q + 3] * v[4 * q + 3];
+                xp[q] = xv;
+            }
+        }
+    }
+}
+
 // ---------------------------------------------------------------- MFMA GEMM
 constexpr int BM = 128, BN = 128, BKB = 128;   // tile rows, cols, K bytes
 constexpr int LDS_STRIDE = BKB + 16;           // padded row (bytes): conflict-free 16-byte reads
 constexpr int NTHREADS = 256;
 
-template <bool I8>
+template <bool I8, int EV>
 __global__ void __launch_bounds__(NTHREADS, 2)
 gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
                  int64_t M, int64_t N, int64_t Kb, EpiParams ep) {
@@ -78,17 +154,15 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
     const int wm = wave / 2, wn = wave % 2;
 
     // global -> register staging: 4 chunks of 16 bytes per operand per thread
-    uint4 ra[4], rb[4];
+    v4i ra[4], rb[4];
     auto gload = [&](int64_t kb0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int c = tid + i * NTHREADS;
             const int r = c / (BKB / 16), col = (c % (BKB / 16)) * 16;
             const int64_t gm = m0 + r, gn = n0 + r;
-            ra[i] = gm < M ? *reinterpret_cast<const uint4*>(A + gm * lda_b + kb0 + col)
-                           : make_uint4(0, 0, 0, 0);
-            rb[i] = gn < N ? *reinterpret_cast<const uint4*>(W + gn * Kb + kb0 + col)
-                           : make_uint4(0, 0, 0, 0);
+            ra[i] = gm < M ? *reinterpret_cast<const v4i*>(A + gm * lda_b + kb0 + col) : v4i{0, 0, 0, 0};
+            rb[i] = gn < N ? *reinterpret_cast<const v4i*>(W + gn * Kb + kb0 + col) : v4i{0, 0, 0, 0};
         }
     };
     auto sstore = [&](int buf) {
@@ -96,8 +170,8 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
         for (int i = 0; i < 4; ++i) {
             const int c = tid + i * NTHREADS;
             const int r = c / (BKB / 16), col = (c % (BKB / 16)) * 16;
-            *reinterpret_cast<uint4*>(&As[buf][r * LDS_STRIDE + col]) = ra[i];
-            *reinterpret_cast<uint4*>(&Bs[buf][r * LDS_STRIDE + col]) = rb[i];
+            *reinterpret_cast<v4i*>(&As[buf][r * LDS_STRIDE + col]) = ra[i];
+            *reinterpret_cast<v4i*>(&Bs[buf][r * LDS_STRIDE + col]) = rb[i];
         }
     };
 
@@ -117,16 +191,14 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
         if (kt + 1 < nk) gload((int64_t)(kt + 1) * BKB);
 #pragma unroll
         for (int ks = 0; ks < BKB / 64; ++ks) {
-            uint4 af[4], bf[4];
+            v4i af[4], bf[4];
             const int koff = ks * 64 + (lane / 16) * 16;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const uint4*>(
-                    &As[buf][(wm * 64 + i * 16 + lane % 16) * LDS_STRIDE + koff]);
+                af[i] = *reinterpret_cast<const v4i*>(&As[buf][(wm * 64 + i * 16 + lane % 16) * LDS_STRIDE + koff]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const uint4*>(
-                    &Bs[buf][(wn * 64 + j * 16 + lane % 16) * LDS_STRIDE + koff]);
+                bf[j] = *reinterpret_cast<const v4i*>(&Bs[buf][(wn * 64 + j * 16 + lane % 16) * LDS_STRIDE + koff]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -159,36 +231,286 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
                     if constexpr (I8) {
                         const int32_t a = acc[i][j][r];
                         const float v = (float)a * ep.a_scale[m] * ep.w_scale[n];
-                        epilogue(ep, m, n, v, a);
+                        epilogue<EV>(ep, m, n, v, a);
                     } else {
-                        epilogue(ep, m, n, acc[i][j][r], 0);
+                        epilogue<EV>(ep, m, n, acc[i][j][r], 0);
                     }
                 }
             }
+}
+
+// ---------------------------------------------------------------- large-tile MFMA GEMM
+// 256x256 workgroup tile, 8 waves (2 per SIMD) in a 2 x 4 grid, each wave
+// owning a 128x64 sub-tile: 32 MFMA accumulator tiles of 16x16 held in VGPRs
+// (built with -mllvm -amdgpu-mfma-vgpr-form=1; with accumulators in AGPRs the
+// compiler rotates them through copies every iteration, and each copy waits
+// for the MFMA pipe).  Two waves per SIMD let one wave's MFMAs run while the
+// other waits on LDS.
+// Software pipeline over K steps of 64 bytes with a 3-slot LDS ring: while the
+// MFMAs of step k run from registers, each wave reads the fragments of step
+// k+1 from LDS, writes step k+2 (staged in registers) into LDS and issues the
+// global loads of step k+3.  One barrier per step; the loop body is
+// branch-free so the scheduler can interleave the four streams.
+// LDS has 32 banks (128 bytes per clock).  Rows are 64 bytes; 16-byte chunk c
+// of row r sits at slot c ^ ((r >> 1) & 3), so the eight rows read or written
+// together by one ds_*_b128 phase hit eight different bank groups.
+constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SLOTS = 3, L_THREADS = 512;
+constexpr int L_TILE_BYTES = L_BM * L_BK;               // one operand, one slot
+constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
+
+__device__ __forceinline__ int swz(int r, int c) { return r * L_BK + ((c ^ ((r >> 1) & 3)) << 4); }
+
+template <bool I8, int EV>
+__global__ void __launch_bounds__(L_THREADS, 1)
+gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
+                  int64_t M, int64_t N, int64_t Kb, EpiParams ep) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+    const int tiles_m = (int)((M + L_BM - 1) / L_BM);
+    const int tiles_n = (int)((N + L_BN - 1) / L_BN);
+    const int nblocks = tiles_m * tiles_n;
+    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
+    // range of tiles so that tiles sharing rows of A or W share an L2.
+    int bid = blockIdx.x;
+    const int full = (nblocks / 8) * 8;
+    if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = bid / per_group;
+    const int first_m = g * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (bid % per_group) % gsize;
+    const int tn = (bid % per_group) / gsize;
+    const int64_t m0 = (int64_t)tm * L_BM, n0 = (int64_t)tn * L_BN;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave, wave = tid / kWave;
+    const int wm = wave / 4, wn = wave % 4;
+
+    // Thread t stages chunk (t % 4) of rows t/4 and t/4 + 128 of both operands
+    // (rows beyond M or N are clamped: their products only reach outputs that
+    // are never stored).  32-bit offsets from the uniform bases.
+    const int lrow = tid / 4, lch = tid % 4;
+    uint32_t aoff[2], boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        aoff[i] = (uint32_t)(min(m0 + lrow + 128 * i, M - 1) * lda_b + lch * 16);
+        boff[i] = (uint32_t)(min(n0 + lrow + 128 * i, N - 1) * Kb + lch * 16);
+    }
+    v4i ra[2], rb[2];
+    const int nk = (int)(Kb / L_BK);
+    typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
+    typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
+    const int arow = wm * 128 + lane % 16, brow = wn * 64 + lane % 16, chunk = lane / 16;
+
+#define LG_LOAD(step)                                                                   \
+    do {                                                                                \
+        const uint32_t kb0 = (uint32_t)min((step), nk - 1) * L_BK;                       \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                 \
+            ra[i] = *reinterpret_cast<const v4i*>(A + (aoff[i] + kb0));                 \
+            rb[i] = *reinterpret_cast<const v4i*>(W + (boff[i] + kb0));                 \
+        }                                                                               \
+    } while (0)
+#define LG_STORE(step)                                                                  \
+    do {                                                                                \
+        uint8_t* dst = lds + ((step) % L_SLOTS) * L_STAGE_BYTES;                        \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                 \
+            *reinterpret_cast<v4i*>(dst + swz(lrow + 128 * i, lch)) = ra[i];            \
+            *reinterpret_cast<v4i*>(dst + L_TILE_BYTES + swz(lrow + 128 * i, lch)) = rb[i]; \
+        }                                                                               \
+    } while (0)
+#define LG_FRAGS(step, fa, fb)                                                          \
+    do {                                                                                \
+        const uint8_t* src = lds + ((step) % L_SLOTS) * L_STAGE_BYTES;                  \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
+            fb[j] = *reinterpret_cast<const frag_t*>(src + L_TILE_BYTES + swz(brow + j * 16, chunk)); \
+        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
+            fa[i] = *reinterpret_cast<const frag_t*>(src + swz(arow + i * 16, chunk));   \
+    } while (0)
+#define LG_BARRIER()                                       \
+    do {                                                   \
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); \
+        __builtin_amdgcn_s_barrier();                      \
+    } while (0)
+#define LG_MFMA(fa, fb)                                                                           \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                 \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
+            if constexpr (I8)                                                                     \
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0); \
+            else                                                                                  \
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
+        }
+// interleave: per 8 MFMAs, 3 fragment reads, 1 LDS write, 1 global load
+#define LG_SCHEDULE()                                                  \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                    \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             \
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);             \
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             \
+    }
+
+    acc_t acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+
+    // prologue: steps 0 and 1 into LDS, step 2 in registers, fragments of step 0
+    LG_LOAD(0);
+    LG_STORE(0);
+    LG_LOAD(1);
+    LG_STORE(1);
+    LG_LOAD(2);
+    LG_BARRIER();
+    frag_t fa0[8], fb0[4], fa1[8], fb1[4];
+    LG_FRAGS(0, fa0, fb0);
+
+    // Two steps per iteration so the fragment double buffer needs no copies.
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+        LG_STORE(kt + 2);
+        LG_LOAD(kt + 3);
+        LG_FRAGS(kt + 1, fa1, fb1);
+        LG_MFMA(fa0, fb0);
+        LG_SCHEDULE();
+        LG_BARRIER();
+        LG_STORE(kt + 3);
+        LG_LOAD(kt + 4);
+        LG_FRAGS(kt + 2, fa0, fb0);
+        LG_MFMA(fa1, fb1);
+        LG_SCHEDULE();
+        LG_BARRIER();
+    }
+    if (kt < nk) {
+        LG_MFMA(fa0, fb0);
+    }
+    __syncthreads();
+#undef LG_LOAD
+#undef LG_STORE
+#undef LG_FRAGS
+#undef LG_BARRIER
+#undef LG_MFMA
+#undef LG_SCHEDULE
+
+    // Epilogue: for each 16-row slab i, every wave parks its 16 x 64 slab of
+    // accumulators in its own LDS region, then each lane finishes 16
+    // consecutive columns of one row.
+    constexpr int EP_STRIDE = 64 + 4;   // words per slab row (padded)
+    float* slab = reinterpret_cast<float*>(lds) + wave * 16 * EP_STRIDE;
+    const int er = lane / 4, ec = (lane % 4) * 16;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (I8)
+                    reinterpret_cast<int32_t*>(slab)[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] =
+                        acc[i][j][r];
+                else
+                    slab[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const int64_t m = m0 + wm * 128 + i * 16 + er;
+        const int64_t n = n0 + wn * 64 + ec;
+        float v[16];
+        int32_t ai[16];
+        if (m < M && n < N) {
+            if constexpr (I8) {
+                const float sa = ep.a_scale[m];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4i t = *reinterpret_cast<const v4i*>(
+                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                    const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ai[4 * q + e] = t[e];
+                        v[4 * q + e] = (float)t[e] * sa * sw[e];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const v4f t = *reinterpret_cast<const v4f*>(slab + er * EP_STRIDE + ec + 4 * q);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[4 * q + e] = t[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) ai[e] = 0;
+            }
+            epilogue16<EV>(ep, m, n, v, ai);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
+constexpr int kNumCU = 256;
+constexpr size_t L_LDS = (size_t)L_SLOTS * L_STAGE_BYTES;
+
+static bool use_large(int64_t M, int64_t N) {
+    const int64_t tiles = ((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN);
+    return tiles >= kNumCU;
+}
+
+static unsigned large_grid(int64_t M, int64_t N) {
+    return (unsigned)(((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN));
 }
 
 static unsigned gemm_grid(int64_t M, int64_t N) {
     return (unsigned)(((M + BM - 1) / BM) * ((N + BN - 1) / BN));
 }
 
+static int variant(const EpiParams& ep) {
+    if (ep.kind == EPI_GELU) return EV_GELU;
+    if (ep.kind == EPI_RESID) return EV_RESID;
+    return ep.acc_out ? EV_STORE_ACC : EV_STORE;
+}
+
+template <bool I8, int EV>
+static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
+                        const EpiParams& ep, hipStream_t st) {
+    if (use_large(M, N) && lda_b % 16 == 0) {
+        static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
+        if (!lds_set) {
+            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
+            lds_set = true;
+        }
+        gemm_large_kernel<I8, EV><<<large_grid(M, N), L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep);
+    }
+    else
+        gemm_mfma_kernel<I8, EV><<<gemm_grid(M, N), NTHREADS, 0, st>>>(a, lda_b, w, M, N, Kb, ep);
+}
+
+template <bool I8>
+static void launch_mfma_any(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
+                            const EpiParams& ep, hipStream_t st) {
+    switch (variant(ep)) {
+        case EV_STORE: launch_mfma<I8, EV_STORE>(a, lda_b, w, M, N, Kb, ep, st); break;
+        case EV_STORE_ACC: launch_mfma<I8, EV_STORE_ACC>(a, lda_b, w, M, N, Kb, ep, st); break;
+        case EV_GELU: launch_mfma<I8, EV_GELU>(a, lda_b, w, M, N, Kb, ep, st); break;
+        default: launch_mfma<I8, EV_RESID>(a, lda_b, w, M, N, Kb, ep, st); break;
+    }
+}
+
 hipError_t launch_gemm_i8(const int8_t* a, const int8_t* w, int64_t M, int64_t N, int64_t K,
                           const EpiParams& ep, hipStream_t st) {
     if (M == 0) return hipSuccess;
-    gemm_mfma_kernel<true><<<gemm_grid(M, N), NTHREADS, 0, st>>>(
-        (const uint8_t*)a, K, (const uint8_t*)w, M, N, K, ep);
+    launch_mfma_any<true>((const uint8_t*)a, K, (const uint8_t*)w, M, N, K, ep, st);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_bf16(const void* a, int64_t lda, const void* w, int64_t M, int64_t N,
                             int64_t K, const EpiParams& ep, hipStream_t st) {
     if (M == 0) return hipSuccess;
-    gemm_mfma_kernel<false><<<gemm_grid(M, N), NTHREADS, 0, st>>>(
-        (const uint8_t*)a, lda * 2, (const uint8_t*)w, M, N, K * 2, ep);
+    launch_mfma_any<false>((const uint8_t*)a, lda * 2, (const uint8_t*)w, M, N, K * 2, ep, st);
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- fp32 GEMM
 // 64x64 tile, 256 threads, 4x4 outputs per thread, K step 16, plain FMA.
+template <int EV>
 __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ W, int64_t M,
                                                        int64_t N, int64_t K, EpiParams ep) {
@@ -227,7 +549,7 @@ __global__ void __launch_bounds__(256) gemm_f32_kernel(const float* __restrict__
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t m = m0 + tm * 4 + i, n = n0 + tn * 4 + j;
-            if (m < M && n < N) epilogue(ep, m, n, acc[i][j], 0);
+            if (m < M && n < N) epilogue<EV>(ep, m, n, acc[i][j], 0);
         }
 }
 
@@ -235,7 +557,11 @@ hipError_t launch_gemm_f32(const float* a, int64_t lda, const float* w, int64_t 
                            int64_t K, const EpiParams& ep, hipStream_t st) {
     if (M == 0) return hipSuccess;
     dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 63) / 64));
-    gemm_f32_kernel<<<grid, 256, 0, st>>>(a, lda, w, M, N, K, ep);
+    switch (variant(ep)) {
+        case EV_GELU: gemm_f32_kernel<EV_GELU><<<grid, 256, 0, st>>>(a, lda, w, M, N, K, ep); break;
+        case EV_RESID: gemm_f32_kernel<EV_RESID><<<grid, 256, 0, st>>>(a, lda, w, M, N, K, ep); break;
+        default: gemm_f32_kernel<EV_STORE><<<grid, 256, 0, st>>>(a, lda, w, M, N, K, ep); break;
+    }
     return hipGetLastError();
 }
 

@@ -168,6 +168,18 @@ def test_block_w8a8_1024px_full_size_sampled():
     _sampled_rows_check(w, wt, inp, out, rows, cos_sin=cs)
 
 
+def test_block_bf16_1024px_full_size_sampled():
+    """bf16 mode at 4352 rows (large-tile GEMM path for every epilogue)."""
+    w = ditsynth.custom("bf16_1024", 4096, 32, 16384, 256, [(64, 64)], "bf16", 35)
+    wt = ditsynth.block_weights(w, 0)
+    inp = ditsynth.block_inputs(w)
+    gb = GpuBlock(w, wt)
+    out = gb.run(inp["x"], inp["mod"], inp["mod_of_seg"])
+    rows = np.array([0, 255, 256, 3000, 4351])
+    cs = oracle.rope_tables(oracle.rope_positions(w.text, w.images))
+    _sampled_rows_check(w, wt, inp, out, rows, cos_sin=cs)
+
+
 def test_block_w8a8_2048px_edit_two_steps_sampled():
     """Prefix K/V written by the uncached step 1 and reused by the cached step 2."""
     w = ditsynth.workload(4)

@@ -44,7 +44,8 @@ def test_quantize_outlier_weights_bit_exact():
     assert w.outliers
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (77, 272, 384), (300, 512, 4096), (129, 128, 16384)])
+@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (77, 272, 384), (300, 512, 4096), (129, 128, 16384),
+                                   (4429, 4144, 256), (4096, 4096, 640)])
 def test_w8a8_linear_exact_accumulators(M, N, K):
     say("w8a8", M, N, K)
     a, b, sa, sb, bias = ditsynth.int8_operands(M, N, K, seed=M * 7 + N)
@@ -88,7 +89,7 @@ def test_w8a8_linear_full_shapes_sampled():
         assert np.all(np.abs(host(y)[ms, ns] - yref) <= bf16_ulp(yref) / 2 + f32_err)
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 64, 64), (100, 272, 640), (320, 4096, 4096)])
+@pytest.mark.parametrize("M,N,K", [(5, 64, 64), (100, 272, 640), (320, 4096, 4096), (4429, 4144, 192)])
 def test_bf16_linear(M, N, K):
     say("bf16 linear", M, N, K)
     rng = np.random.default_rng(M + N)
