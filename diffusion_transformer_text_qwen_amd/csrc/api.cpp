@@ -223,7 +223,9 @@ int block_causal_attention(const void* q, const void* k, const void* v, void* o,
     if (sm_scale <= 0.0f) sm_scale = 1.0f / std::sqrt((float)d);
     const AttnSegs segs = make_attn_segs(seg_len, n_seg);
     if (dtype == DIT_BF16) {
-        CHECK((T_q + 127) / 128 < 0x7fffffff, DIT_E_UNSUPPORTED, "T_q too large");
+        CHECK(T_k < ((int64_t)1 << 31) && ldq < ((int64_t)1 << 31) && ldk < ((int64_t)1 << 31) &&
+                  ldv < ((int64_t)1 << 31) && ldo < ((int64_t)1 << 31),
+              DIT_E_UNSUPPORTED, "bf16 attention needs T_k and strides below 2^31");
         RUN(launch_attention_bf16(q, k, v, o, T_q, T_k, H, ldq, ldk, ldv, ldo, segs, sm_scale, S(stream)),
             "attention_bf16");
     } else {
@@ -486,10 +488,12 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     RUN(launch_adaln(x, bf, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
         "adaln2");
     }
-    // S8: MLP up + GELU
+    // S8: MLP up + GELU.  W8A8: the up GEMM stores u (bf16) and the GELU is
+    // applied in the HBM-bound quantization pass of S9, which has spare ALU;
+    // otherwise the GELU runs in the GEMM epilogue.
     {
         EpiParams ep{};
-        ep.kind = EPI_GELU;
+        ep.kind = q8 ? EPI_STORE : EPI_GELU;
         ep.act_bf16 = bf;
         ep.y_bf16 = bf;
         ep.bias = w->b_1;
@@ -498,10 +502,10 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
         ProfScope ps(DIT_SITE_UP_GEMM, st);
         RUN(gemm(h, a8, sa, w->w_1, w->s_1, F, D, ep), "up_gemm");
     }
-    // S9 + S10: quantize g, MLP down with gated residual into x
+    // S9 + S10: (GELU +) quantize g, MLP down with gated residual into x
     if (q8) {
         ProfScope ps(DIT_SITE_QUANT_G, st);
-        RUN(launch_quantize_rows(gb, true, T, F, F, g8, sg, st), "quantize_g");
+        RUN(launch_gelu_quantize_rows(gb, T, F, g8, sg, st), "gelu_quantize_g");
     }
     {
         EpiParams ep{};

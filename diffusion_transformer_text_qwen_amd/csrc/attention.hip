@@ -21,8 +21,15 @@ namespace dit {
 
 constexpr int AQ = 128;                 // queries per workgroup
 constexpr int AK = 64;                  // keys per tile
-constexpr int KS_STRIDE = 128 * 2 + 16; // bytes per key row of the K tile
-constexpr int VT_STRIDE = AK * 2 + 8;   // bytes per d row of the transposed V tile
+constexpr int KS_STRIDE = 128 * 2 + 16; // bytes per key row of the K tile (272 = 16 mod 128:
+                                        // eight rows read together hit eight bank groups)
+constexpr int VT_STRIDE = AK * 2;       // bytes per d row of the transposed V tile
+constexpr int KS_BYTES = AK * KS_STRIDE;
+constexpr int VT_BYTES = 128 * VT_STRIDE;
+constexpr int ABUF_BYTES = KS_BYTES + VT_BYTES;
+// Rescale threshold of the online softmax, in log2 units: the running max is
+// only raised when a tile's max exceeds it by more than this, so P <= 2^8.
+constexpr float kRescaleLog2 = 8.0f;
 
 // Keys visible to a query at absolute position pos: [0, end of its segment).
 // Static indices only (keeps the argument struct out of private memory).
@@ -34,81 +41,88 @@ __device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
     return e;
 }
 
+// Transposed V tile: element (d, key) lives in 8-byte slot (key/4) ^ vt_swz(d)
+// of row d.  Conflict-free for both the transposing writes (16 lanes with d
+// spaced by 8) and the MFMA operand reads (16 lanes with consecutive d).
+__device__ __forceinline__ int vt_addr(int d, int kc) { return d * VT_STRIDE + ((kc ^ ((2 * d + (d >> 3)) & 15)) << 3); }
+
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
-                 const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int64_t T_q, int64_t T_k,
-                 int64_t ldq, int64_t ldk, int64_t ldv, int64_t ldo, AttnSegs sg, float c_log2) {
-    __shared__ __attribute__((aligned(16))) uint8_t Ks[AK * KS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint8_t Vt[128 * VT_STRIDE];
+                 const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int T_q, int T_k,
+                 int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ABUF_BYTES];
 
-    const int nqb = (int)((T_q + AQ - 1) / AQ);
+    const int nqb = (T_q + AQ - 1) / AQ;
     const int qb = nqb - 1 - (int)blockIdx.x;   // longest key ranges first
     const int h = blockIdx.y;
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int hh = lane / 32, lq = lane % 32;
-    const int64_t off = T_k - T_q;
+    const int off = T_k - T_q;
 
-    const int64_t q_first = (int64_t)qb * AQ;
-    const int64_t q_last = min(q_first + AQ, T_q) - 1;
-    const int64_t kv_min = kv_end_of(sg, off + q_first);
-    const int64_t kv_hi = kv_end_of(sg, off + q_last);
+    const int q_first = qb * AQ;
+    const int q_last = min(q_first + AQ, T_q) - 1;
+    const int kv_min = (int)kv_end_of(sg, off + q_first);
+    const int kv_hi = (int)kv_end_of(sg, off + q_last);
 
-    const int64_t qi = q_first + wave * 32 + lq;   // this lane's query
+    const int qi = q_first + wave * 32 + lq;   // this lane's query
     const bool q_ok = qi < T_q;
-    const int64_t my_end = q_ok ? kv_end_of(sg, off + qi) : T_k;
+    const int my_end = q_ok ? (int)kv_end_of(sg, off + qi) : T_k;
 
     // Q^T fragments (B operand): Q[qi][kb*16 + hh*8 .. +7]
     v8bf qf[8];
+    {
+        const __bf16* qrow = Q + (size_t)(q_ok ? qi : 0) * ldq + h * 128 + hh * 8;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        if (q_ok)
-            qf[kb] = *reinterpret_cast<const v8bf*>(Q + qi * ldq + (int64_t)h * 128 + kb * 16 + hh * 8);
-        else
-            qf[kb] = v8bf{};
+        for (int kb = 0; kb < 8; ++kb) qf[kb] = q_ok ? *reinterpret_cast<const v8bf*>(qrow + kb * 16) : v8bf{};
     }
+
+    // global -> register staging of one K/V tile: K: keys c/16 (+16 i), chunk
+    // c%16; V: keys 4*kg .. 4*kg+3, d-chunk dc.
+    const int kkey = tid / 16, kch = tid % 16;
+    const int dc = tid % 16, kg = tid / 16;
+    const __bf16* kbase = Kg + h * 128 + kch * 8;
+    const __bf16* vbase = Vg + h * 128 + dc * 8;
+    v4i rk[4], rv[4];
+    auto gload = [&](int j0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int gk = j0 + kkey + 16 * i;
+            rk[i] = gk < T_k ? *reinterpret_cast<const v4i*>(kbase + (size_t)gk * ldk) : v4i{0, 0, 0, 0};
+            const int gv = j0 + kg * 4 + i;
+            rv[i] = gv < T_k ? *reinterpret_cast<const v4i*>(vbase + (size_t)gv * ldv) : v4i{0, 0, 0, 0};
+        }
+    };
+    auto sstore = [&](int buf) {
+        uint8_t* ks = lds + buf * ABUF_BYTES;
+        uint8_t* vt = ks + KS_BYTES;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *reinterpret_cast<v4i*>(ks + (kkey + 16 * i) * KS_STRIDE + kch * 16) = rk[i];
+        // transpose: 4 keys x 8 dims -> 8 rows (d) of 4 keys
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int w = r / 2, sh = (r % 2) * 16;
+            uint2 packed;
+            packed.x = ((uint32_t)rv[0][w] >> sh & 0xFFFFu) | (((uint32_t)rv[1][w] >> sh & 0xFFFFu) << 16);
+            packed.y = ((uint32_t)rv[2][w] >> sh & 0xFFFFu) | (((uint32_t)rv[3][w] >> sh & 0xFFFFu) << 16);
+            *reinterpret_cast<uint2*>(vt + vt_addr(dc * 8 + r, kg)) = packed;
+        }
+    };
 
     v16f oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = v16f{};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    const int ntiles = (int)((kv_hi + AK - 1) / AK);
+    const int ntiles = (kv_hi + AK - 1) / AK;
+    gload(0);
+    sstore(0);
+    if (ntiles > 1) gload(AK);
+    __syncthreads();
     for (int t = 0; t < ntiles; ++t) {
-        const int64_t j0 = (int64_t)t * AK;
-        __syncthreads();
-        // K tile: 64 keys x 256 bytes, 16-byte chunks
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int c = tid + i * 256;
-            const int key = c / 16, ch = c % 16;
-            const int64_t gk = j0 + key;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (gk < T_k) val = *reinterpret_cast<const uint4*>(Kg + gk * ldk + (int64_t)h * 128 + ch * 8);
-            *reinterpret_cast<uint4*>(&Ks[key * KS_STRIDE + ch * 16]) = val;
-        }
-        // V tile transposed: thread owns d-chunk dc (8 dims) of keys 4kg..4kg+3
-        {
-            const int dc = tid % 16, kg = tid / 16;
-            uint4 rv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t gk = j0 + kg * 4 + i;
-                rv[i] = gk < T_k ? *reinterpret_cast<const uint4*>(Vg + gk * ldv + (int64_t)h * 128 + dc * 8)
-                                 : make_uint4(0, 0, 0, 0);
-            }
-            const uint16_t* e0 = reinterpret_cast<const uint16_t*>(&rv[0]);
-            const uint16_t* e1 = reinterpret_cast<const uint16_t*>(&rv[1]);
-            const uint16_t* e2 = reinterpret_cast<const uint16_t*>(&rv[2]);
-            const uint16_t* e3 = reinterpret_cast<const uint16_t*>(&rv[3]);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                uint2 packed;
-                packed.x = (uint32_t)e0[r] | ((uint32_t)e1[r] << 16);
-                packed.y = (uint32_t)e2[r] | ((uint32_t)e3[r] << 16);
-                *reinterpret_cast<uint2*>(&Vt[(dc * 8 + r) * VT_STRIDE + kg * 8]) = packed;
-            }
-        }
-        __syncthreads();
+        const int j0 = t * AK;
+        const uint8_t* ks = lds + (t & 1) * ABUF_BYTES;
+        const uint8_t* vt = ks + KS_BYTES;
 
         // S^T = K Q^T : two 32-key halves
         v16f sacc[2];
@@ -117,10 +131,14 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
             sacc[kh] = v16f{};
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb) {
-                const v8bf a = *reinterpret_cast<const v8bf*>(
-                    &Ks[(kh * 32 + lq) * KS_STRIDE + kb * 32 + hh * 16]);
+                const v8bf a = *reinterpret_cast<const v8bf*>(ks + (kh * 32 + lq) * KS_STRIDE + kb * 32 + hh * 16);
                 sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], sacc[kh], 0, 0, 0);
             }
+        }
+        // stage the next tile while this one is consumed
+        if (t + 1 < ntiles) {
+            sstore((t + 1) & 1);
+            if (t + 2 < ntiles) gload(j0 + 2 * AK);
         }
         // mask keys beyond this query's visible prefix (only tiles that cross it)
         if (j0 + AK > kv_min) {
@@ -128,7 +146,7 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
             for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int64_t key = j0 + kh * 32 + (j / 4) * 8 + hh * 4 + (j % 4);
+                    const int key = j0 + kh * 32 + (j / 4) * 8 + hh * 4 + (j % 4);
                     if (key >= my_end) sacc[kh][j] = -INFINITY;
                 }
         }
@@ -138,45 +156,52 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
 #pragma unroll
             for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f((m_run - m_new) * c_log2);
-        const float mb = m_new * c_log2;
+        // lazy rescale: raise the running max only when this tile exceeds it by
+        // more than 2^kRescaleLog2 (wave-uniform decision)
+        if (__any((mx - m_run) * c_log2 > kRescaleLog2)) {
+            const float m_new = fmaxf(m_run, mx);
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+            l_run *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+            m_run = m_new;
+        }
+        const float mb = m_run * c_log2;
         float psum = 0.0f;
         v8bf pb[4];
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
-                const float p = exp2f(fmaf(sacc[kh][j], c_log2, -mb));
+                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kh][j], c_log2, -mb));
                 psum += p;
                 pb[kh * 2 + j / 8][j % 8] = to_bf16(p);
             }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+        l_run += psum;
 
         // O^T += V^T P^T, 16 keys per MFMA in the S^T lane order
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const uint8_t* row = &Vt[(dt * 32 + lq) * VT_STRIDE];
-                const uint2 lo = *reinterpret_cast<const uint2*>(row + (16 * b + hh * 4) * 2);
-                const uint2 hi = *reinterpret_cast<const uint2*>(row + (16 * b + 8 + hh * 4) * 2);
-                uint4 av = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<v8bf*>(&av), pb[b],
-                                                                   oacc[dt], 0, 0, 0);
+                const int d = dt * 32 + lq;
+                const uint2 lo = *reinterpret_cast<const uint2*>(vt + vt_addr(d, 4 * b + hh));
+                const uint2 hi = *reinterpret_cast<const uint2*>(vt + vt_addr(d, 4 * b + 2 + hh));
+                v4i av = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<v8bf*>(&av), pb[b], oacc[dt],
+                                                                   0, 0, 0);
             }
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
     if (!q_ok) return;
     const float inv = 1.0f / l_tot;
-    __bf16* orow = O + qi * ldo + (int64_t)h * 128;
+    __bf16* orow = O + (size_t)qi * ldo + h * 128;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -195,7 +220,8 @@ hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, vo
     const float c = sm_scale * 1.4426950408889634f;
     dim3 grid((unsigned)((T_q + AQ - 1) / AQ), (unsigned)H);
     attn_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
-                                           (__bf16*)o, T_q, T_k, ldq, ldk, ldv, ldo, segs, c);
+                                           (__bf16*)o, (int)T_q, (int)T_k, (int)ldq, (int)ldk, (int)ldv,
+                                           (int)ldo, segs, c);
     return hipGetLastError();
 }
 

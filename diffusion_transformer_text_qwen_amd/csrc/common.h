@@ -78,6 +78,16 @@ __device__ __forceinline__ int seg_set(const SegMap& sm, int64_t row) {
     return set;
 }
 
+// tanh-approximated GELU, 0.5 u (1 + tanh(k (u + 0.044715 u^3))) with
+// k = sqrt(2/pi), evaluated as u * sigmoid(2 k (u + 0.044715 u^3)) (the same
+// function: 0.5 (1 + tanh(x)) = 1 / (1 + exp(-2x))) with the hardware exp and
+// reciprocal (a few ulp in fp32, far below the bf16 rounding that follows).
+__device__ __forceinline__ float gelu_tanh_fast(float u) {
+    const float z = 1.5957691216057308f * u * fmaf(0.044715f * u, u, 1.0f);
+    const float e = __expf(-z);
+    return u * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
 // Symmetric int8 code of v for scale s (s == 0 -> 0); IEEE fp32 division,
 // ties to even.
 __device__ __forceinline__ int8_t quant_code(float v, float s) {

@@ -9,7 +9,9 @@ namespace dit {
 // ---------------------------------------------------------------- quantization
 // One 256-thread workgroup per row.  The row is read once into registers as
 // 16-byte chunks (8 bf16 or 4 f32 values), reduced to amax, then coded.
-template <typename T, int MAXC>
+// GELU_PRE: the row holds the bf16 MLP up-projection u; the quantized value is
+// g = bf16(GELU_tanh(u)) (the MLP activation fused into its quantization pass).
+template <typename T, int MAXC, bool GELU_PRE = false>
 __global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict__ x, int64_t K,
                                                             int64_t ldx, int8_t* __restrict__ q,
                                                             float* __restrict__ scale) {
@@ -25,7 +27,11 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict_
         const int c = threadIdx.x + i * 256;
         if (c < nchunk) {
             buf[i] = *reinterpret_cast<const uint4*>(xr + (int64_t)c * E);
-            const T* v = reinterpret_cast<const T*>(&buf[i]);
+            T* v = reinterpret_cast<T*>(&buf[i]);
+            if constexpr (GELU_PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) v[e] = from_f<T>(gelu_tanh_fast(to_f<T>(v[e])));
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) amax = fmaxf(amax, fabsf(to_f<T>(v[e])));
         }
@@ -71,6 +77,18 @@ hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, 
             quantize_rows_kernel<float, 16><<<dim3((unsigned)M), dim3(256), 0, st>>>(
                 (const float*)x, K, ldx, q, scale);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
+                                     hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (K / 8 <= 256 * 4)
+        quantize_rows_kernel<__bf16, 4, true><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+            (const __bf16*)u, K, K, q, scale);
+    else
+        quantize_rows_kernel<__bf16, 16, true><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+            (const __bf16*)u, K, K, q, scale);
     return hipGetLastError();
 }
 

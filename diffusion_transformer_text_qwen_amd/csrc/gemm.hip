@@ -10,10 +10,7 @@
 
 namespace dit {
 
-__device__ __forceinline__ float gelu_tanh(float u) {
-    const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * u * (1.0f + tanhf(k0 * (u + 0.044715f * u * u * u)));
-}
+__device__ __forceinline__ float gelu_tanh(float u) { return gelu_tanh_fast(u); }
 
 // Epilogue variants, fixed per kernel instantiation (keeps one path live).
 enum EpiVariant : int { EV_STORE = 0, EV_STORE_ACC = 1, EV_GELU = 2, EV_RESID = 3 };

@@ -41,6 +41,8 @@ hipError_t launch_gemm_f32(const float* a, int64_t lda, const float* w, int64_t 
 
 hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, float* scale, hipStream_t st);
+hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
+                                     hipStream_t st);
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                         const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
                         float* qs, hipStream_t st);
