@@ -53,8 +53,9 @@ _SIGS = {
     "dit_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dit_last_error": ([], ctypes.c_char_p),
     "dit_quantize_rows": ([_vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp], ctypes.c_int),
-    "w8a8_linear": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp, _vp],
-                    ctypes.c_int),
+    "w8a8_linear_workspace_bytes": ([], ctypes.c_size_t),
+    "w8a8_linear": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp, _vp,
+                     ctypes.c_size_t, _vp], ctypes.c_int),
     "bf16_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp],
                     ctypes.c_int),
     "f32_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _c_i64, _vp], ctypes.c_int),
@@ -131,11 +132,16 @@ def quantize_rows(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=
            "dit_quantize_rows")
 
 
-def w8a8_linear(a, a_scale, w, w_scale, bias, y, acc_out=None, stream=None) -> None:
+def w8a8_linear_workspace_bytes() -> int:
+    return int(lib().w8a8_linear_workspace_bytes())
+
+
+def w8a8_linear(a, a_scale, w, w_scale, bias, y, acc_out=None, workspace=None, stream=None) -> None:
     M, K = a.shape
     N = w.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().w8a8_linear(_p(a), _p(a_scale), M, K, _p(w), _p(w_scale), _p(bias), N, _p(y), _dt(y),
-                             y.stride(0), _p(acc_out), _stream(stream)), "w8a8_linear")
+                             y.stride(0), _p(acc_out), _p(workspace), wsb, _stream(stream)), "w8a8_linear")
 
 
 def bf16_linear(a, w, bias, y, stream=None) -> None:

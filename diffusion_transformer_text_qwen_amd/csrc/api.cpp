@@ -153,23 +153,34 @@ int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
     return DIT_OK;
 }
 
+size_t w8a8_linear_workspace_bytes(void) { return (size_t)kSplitPartialBytes; }
+
 int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
                 const float* w_scale, const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy,
-                int32_t* acc_out, void* stream) {
+                int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
     CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
     CHECK(M >= 0 && K >= 1 && N >= 1 && ldy >= N, DIT_E_SHAPE, "need M>=0, K>=1, N>=1, ldy>=N");
     CHECK(K % 128 == 0, DIT_E_UNSUPPORTED, "K=%lld must be a multiple of 128", (long long)K);
     CHECK(N % 16 == 0, DIT_E_UNSUPPORTED, "N=%lld must be a multiple of 16", (long long)N);
     CHECK(K <= kMaxK8, DIT_E_UNSUPPORTED, "K=%lld beyond the int32-safe bound", (long long)K);
     CHECK(((M + 127) / 128) * ((N + 127) / 128) < 0x7fffffff, DIT_E_UNSUPPORTED, "too many tiles");
+    CHECK(M * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), DIT_E_UNSUPPORTED,
+          "operands must be below 2 GiB");
+    CHECK(workspace == nullptr || workspace_bytes >= w8a8_linear_workspace_bytes(), DIT_E_WORKSPACE,
+          "workspace needs %zu bytes", w8a8_linear_workspace_bytes());
     if (M == 0) return DIT_OK;
     CHECK(a && a_scale && w && w_scale && y, DIT_E_NULL, "a, a_scale, w, w_scale and y must be non-NULL");
     CHECK(aligned16(a) && aligned16(w), DIT_E_ALIGN, "a and w must be 16-byte aligned");
+    CHECK(workspace == nullptr || aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
     EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
     ep.a_scale = a_scale;
     ep.w_scale = w_scale;
     ep.acc_out = acc_out;
     ep.ldacc = N;
+    if (workspace) {
+        ep.split_partial = (int32_t*)workspace;
+        ep.split_bytes = kSplitPartialBytes;
+    }
     RUN(launch_gemm_i8(a, w, M, N, K, ep, S(stream)), "w8a8_linear");
     return DIT_OK;
 }
@@ -318,7 +329,7 @@ int dit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* 
 namespace {
 
 struct Plan {
-    size_t h, a8, sa, qkv, q, o, o8, so, g, g8, sg, total;
+    size_t h, a8, sa, qkv, q, o, o8, so, g, g8, sg, split, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -345,6 +356,7 @@ Plan plan(const dit_block_config* cfg, int64_t T) {
     p.g = take(T * F * act);
     p.g8 = take(q8 ? T * F : 0);
     p.sg = take(q8 ? T * 4 : 0);
+    p.split = take(q8 ? (size_t)kSplitPartialBytes : 0);
     p.total = off;
     return p;
 }
@@ -421,12 +433,15 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     uint8_t* kc = (uint8_t*)k_cache + (size_t)row_off * D * act;
     uint8_t* vc = (uint8_t*)v_cache + (size_t)row_off * D * act;
 
+    int32_t* split_partial = (int32_t*)(ws + p.split);
     auto gemm = [&](const void* A, const int8_t* A8, const float* As, const void* Wt, const float* Ws,
                     int64_t N, int64_t K, const EpiParams& ep) -> hipError_t {
         if (q8) {
             EpiParams e = ep;
             e.a_scale = As;
             e.w_scale = Ws;
+            e.split_partial = split_partial;
+            e.split_bytes = kSplitPartialBytes;
             return launch_gemm_i8(A8, (const int8_t*)Wt, T, N, K, e, st);
         }
         if (bf) return launch_gemm_bf16(A, K, Wt, T, N, K, ep, st);

@@ -5,6 +5,8 @@
 // The two MFMA kernels share one byte-level tiling: a 16-byte operand slice per
 // lane covers 16 int8 or 8 bf16 values of one row, so a 128-byte K step is two
 // MFMA K steps for either type.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -257,20 +259,41 @@ constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * L_BK + ((c ^ ((r >> 1) & 3)) << 4); }
 
+// Remainder split-K: with T tiles on C compute units, floor(T/C)*C tiles run
+// whole in one launch; each of the r remaining tiles is split into S K ranges
+// run by S workgroups of a second launch, which store int32 partial sums; a
+// third launch adds them (integer addition: exact in any order) and applies
+// the epilogue.  This fills the otherwise mostly idle last round; kernel
+// boundaries order the partial stores before their reads.
+struct SplitPlan {
+    int32_t tau0;       // first tile (in tile order) of this launch
+    int32_t ntiles;     // tiles of this launch
+    int32_t S;          // 0: whole tiles with epilogue; >= 2: K splits writing partials
+};
+
 template <bool I8, int EV>
 __global__ void __launch_bounds__(L_THREADS, 1)
 gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
-                  int64_t M, int64_t N, int64_t Kb, EpiParams ep) {
+                  int64_t M, int64_t N, int64_t Kb, EpiParams ep, SplitPlan sp) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
 
     const int tiles_m = (int)((M + L_BM - 1) / L_BM);
     const int tiles_n = (int)((N + L_BN - 1) / L_BN);
-    const int nblocks = tiles_m * tiles_n;
-    // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a contiguous
-    // range of tiles so that tiles sharing rows of A or W share an L2.
-    int bid = blockIdx.x;
-    const int full = (nblocks / 8) * 8;
-    if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+    const int nk_all = (int)(Kb / L_BK);
+    // tile order index and K range of this workgroup
+    int bid = blockIdx.x, split = -1, ks0 = 0, nk = nk_all;
+    if (sp.S == 0) {
+        // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
+        // contiguous range of tiles so that tiles sharing rows of A or W share an L2.
+        const int full = (sp.ntiles / 8) * 8;
+        if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
+        bid += sp.tau0;
+    } else {
+        split = bid % sp.S;
+        bid = sp.tau0 + bid / sp.S;
+        ks0 = (int)((int64_t)split * nk_all / sp.S);
+        nk = (int)((int64_t)(split + 1) * nk_all / sp.S) - ks0;
+    }
     constexpr int GROUP = 8;
     const int per_group = GROUP * tiles_n;
     const int g = bid / per_group;
@@ -295,14 +318,13 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         boff[i] = (uint32_t)(min(n0 + lrow + 128 * i, N - 1) * Kb + lch * 16);
     }
     v4i ra[2], rb[2];
-    const int nk = (int)(Kb / L_BK);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
     typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
     const int arow = wm * 128 + lane % 16, brow = wn * 64 + lane % 16, chunk = lane / 16;
 
 #define LG_LOAD(step)                                                                   \
     do {                                                                                \
-        const uint32_t kb0 = (uint32_t)min((step), nk - 1) * L_BK;                       \
+        const uint32_t kb0 = (uint32_t)(ks0 + min((step), nk - 1)) * L_BK;               \
         _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                 \
             ra[i] = *reinterpret_cast<const v4i*>(A + (aoff[i] + kb0));                 \
             rb[i] = *reinterpret_cast<const v4i*>(W + (boff[i] + kb0));                 \
@@ -408,6 +430,20 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
                     slab[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if constexpr (I8) {
+            if (split >= 0) {
+                // partial sums of this K range, row-major 256 x 256 per (tile, split)
+                int32_t* part = ep.split_partial +
+                                ((int64_t)(bid - sp.tau0) * sp.S + split) * (L_BM * L_BN) +
+                                (wm * 128 + i * 16 + er) * L_BN + wn * 64 + ec;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4i*>(part + 4 * q) = *reinterpret_cast<const v4i*>(
+                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                continue;
+            }
+        }
         const int64_t m = m0 + wm * 128 + i * 16 + er;
         const int64_t n = n0 + wn * 64 + ec;
         float v[16];
@@ -464,17 +500,94 @@ static int variant(const EpiParams& ep) {
     return ep.acc_out ? EV_STORE_ACC : EV_STORE;
 }
 
+static int num_cus() {
+    static int n = 0;
+    if (n == 0) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            n = v;
+        else
+            n = kNumCU;
+    }
+    return n;
+}
+
+// Split plan for T tiles of nk K steps: split only the r tiles of the last,
+// partial round into S <= C / r ranges of at least 8 steps each.
+static int plan_split(int64_t tiles, int nk, const EpiParams& ep, int64_t* full) {
+    *full = tiles;
+    if (!ep.split_partial) return 0;
+    const int C = num_cus();
+    const int64_t R = tiles / C, r = tiles - R * C;
+    if (R == 0 || r == 0) return 0;
+    int S = (int)std::min<int64_t>(C / r, 16);
+    S = std::min(S, nk / 8);
+    if (S < 2 || r * S * (int64_t)L_BM * L_BN * 4 > ep.split_bytes) return 0;
+    *full = R * C;
+    return S;
+}
+
+// Sum of the S partial tiles of each split tile, then the int8 epilogue.  One
+// workgroup per 16 rows of a tile; thread t owns 16 consecutive columns.
+template <int EV>
+__global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N, EpiParams ep, int32_t tau0,
+                                                           int32_t S) {
+    const int tiles_m = (int)((M + L_BM - 1) / L_BM);
+    const int tiles_n = (int)((N + L_BN - 1) / L_BN);
+    const int local = blockIdx.x / 16, rb = blockIdx.x % 16;
+    const int tau = tau0 + local;
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = tau / per_group;
+    const int first_m = g * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    const int tm = first_m + (tau % per_group) % gsize;
+    const int tn = (tau % per_group) / gsize;
+    const int row = rb * 16 + threadIdx.x / 16, col = (threadIdx.x % 16) * 16;
+    const int64_t m = (int64_t)tm * L_BM + row, n = (int64_t)tn * L_BN + col;
+    if (m >= M || n >= N) return;
+    v4i sum[4] = {};
+    const int32_t* part = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + row * L_BN + col;
+    for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+    const float sa = ep.a_scale[m];
+    float v[16];
+    int32_t ai[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            ai[4 * q + e] = sum[q][e];
+            v[4 * q + e] = (float)sum[q][e] * sa * sw[e];
+        }
+    }
+    epilogue16<EV>(ep, m, n, v, ai);
+}
+
 template <bool I8, int EV>
 static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                         const EpiParams& ep, hipStream_t st) {
     if (use_large(M, N) && lda_b % 16 == 0) {
-        static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
+        static bool lds_set = false;   // allow 96 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
             (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
             lds_set = true;
         }
-        gemm_large_kernel<I8, EV><<<large_grid(M, N), L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep);
+        const int64_t tiles = large_grid(M, N);
+        int64_t full = tiles;
+        const int S = I8 ? plan_split(tiles, (int)(Kb / L_BK), ep, &full) : 0;
+        gemm_large_kernel<I8, EV><<<(unsigned)full, L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
+                                                                           SplitPlan{0, (int32_t)full, 0});
+        if (S) {
+            const int32_t r = (int32_t)(tiles - full);
+            gemm_large_kernel<I8, EV><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
+                a, lda_b, w, M, N, Kb, ep, SplitPlan{(int32_t)full, r, S});
+            split_reduce_kernel<EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
+        }
     }
     else
         gemm_mfma_kernel<I8, EV><<<gemm_grid(M, N), NTHREADS, 0, st>>>(a, lda_b, w, M, N, Kb, ep);

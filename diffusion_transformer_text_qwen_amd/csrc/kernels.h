@@ -30,7 +30,15 @@ struct EpiParams {
     const float* gate;     // gate row of modulation set 0; set s at gate + s * gate_stride
     int64_t gate_stride;
     SegMap sm;
+    // Remainder split-K scratch (int8 GEMM only; NULL = no split): int32
+    // partial tiles of the split launch, read back by the reduce launch.
+    int32_t* split_partial;
+    int64_t split_bytes;   // capacity of split_partial in bytes
 };
+
+// Bytes of split scratch the int8 GEMM may use for any shape: at most C tiles x
+// 256 x 256 int32 (r * S <= C with C = 256 compute units).
+constexpr int64_t kSplitPartialBytes = (int64_t)256 * 256 * 256 * 4;
 
 hipError_t launch_gemm_i8(const int8_t* a, const int8_t* w, int64_t M, int64_t N, int64_t K,
                           const EpiParams& ep, hipStream_t st);

@@ -77,11 +77,17 @@ int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
  * w_scale [N], bias [N] fp32 or NULL.  y [M, N] with row stride ldy, dtype
  * DIT_BF16 (rounded to nearest even) or DIT_F32.  If acc_out is not NULL the
  * exact int32 sums are also stored there ([M, N], row stride N).
+ * workspace (device, may be NULL): scratch of workspace_bytes >=
+ * w8a8_linear_workspace_bytes() lets the kernel split the K range of the tiles
+ * of a partially filled last round across workgroups (exact: int32 partial
+ * sums); its contents need not be initialized and are left unspecified.
  * Supported: K % 128 == 0, N % 16 == 0, K <= 133144 (so K*127^2 < 2^31).
  */
+size_t w8a8_linear_workspace_bytes(void);
 int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
                 const int8_t* w, const float* w_scale, const float* bias, int64_t N,
-                void* y, int y_dtype, int64_t ldy, int32_t* acc_out, void* stream);
+                void* y, int y_dtype, int64_t ldy, int32_t* acc_out, void* workspace,
+                size_t workspace_bytes, void* stream);
 
 /*
  * bf16 linear for the non-quantized linears: y = a w^T + bias with fp32

@@ -56,14 +56,17 @@ def test_quantize_rows_validation():
 
 def test_linear_validation():
     lib = dq.lib()
-    assert lib.w8a8_linear(16, 16, 4, 100, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 5     # K % 128
-    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 60, 16, dq.BF16, 64, NULL, S) == 5     # N % 16
-    assert lib.w8a8_linear(16, 16, 4, 133248, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 5  # int32 bound
-    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.I8, 64, NULL, S) == 3
-    assert lib.w8a8_linear(NULL, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 1
-    assert lib.w8a8_linear(17, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, S) == 4
-    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 32, NULL, S) == 2     # ldy < N
-    assert lib.w8a8_linear(NULL, NULL, 0, 128, NULL, NULL, NULL, 64, NULL, dq.BF16, 64, NULL, S) == 0
+    W = (NULL, 0)   # no workspace
+    assert lib.w8a8_linear(16, 16, 4, 100, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, *W, S) == 5     # K % 128
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 60, 16, dq.BF16, 64, NULL, *W, S) == 5     # N % 16
+    assert lib.w8a8_linear(16, 16, 4, 133248, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, *W, S) == 5  # int32 bound
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.I8, 64, NULL, *W, S) == 3
+    assert lib.w8a8_linear(NULL, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, *W, S) == 1
+    assert lib.w8a8_linear(17, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, *W, S) == 4
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 32, NULL, *W, S) == 2     # ldy < N
+    assert lib.w8a8_linear(16, 16, 4, 128, 16, 16, NULL, 64, 16, dq.BF16, 64, NULL, 256, 1024, S) == 6  # small ws
+    assert lib.w8a8_linear(NULL, NULL, 0, 128, NULL, NULL, NULL, 64, NULL, dq.BF16, 64, NULL, *W, S) == 0
+    assert lib.w8a8_linear_workspace_bytes() >= 64 << 20
     assert lib.bf16_linear(16, 4, 96, 96, 16, NULL, 64, 16, dq.BF16, 64, S) == 5
     assert lib.bf16_linear(16, 4, 64, 60, 16, NULL, 64, 16, dq.BF16, 64, S) == 2
     assert lib.f32_linear(16, 4, 20, 20, 16, NULL, 64, 16, 64, S) == 5

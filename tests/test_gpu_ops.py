@@ -44,17 +44,21 @@ def test_quantize_outlier_weights_bit_exact():
     assert w.outliers
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 16, 128), (77, 272, 384), (300, 512, 4096), (129, 128, 16384),
-                                   (4429, 4144, 256), (4096, 4096, 640)])
-def test_w8a8_linear_exact_accumulators(M, N, K):
-    say("w8a8", M, N, K)
+@pytest.mark.parametrize("M,N,K,ws", [(1, 16, 128, False), (77, 272, 384, False), (300, 512, 4096, True),
+                                      (129, 128, 16384, False), (4429, 4144, 256, False), (4096, 4096, 640, False),
+                                      (4352, 4096, 1024, True), (4429, 4144, 2048, True)])
+def test_w8a8_linear_exact_accumulators(M, N, K, ws):
+    """ws=True passes a workspace: tiles of a partial last round are split along K
+    (272 / 306 tiles on 256 CUs here), partial int32 sums reduced by the last arriver."""
+    say("w8a8", M, N, K, ws)
     a, b, sa, sb, bias = ditsynth.int8_operands(M, N, K, seed=M * 7 + N)
     acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
     y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
     yf = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    work = torch.full((dq.w8a8_linear_workspace_bytes(),), 0x5A, dtype=torch.uint8, device=DEV) if ws else None
     args = (dev(a, torch.int8), dev(sa), dev(b, torch.int8), dev(sb), dev(bias))
-    dq.w8a8_linear(*args, y, acc_out=acc)
-    dq.w8a8_linear(*args, yf)
+    dq.w8a8_linear(*args, y, acc_out=acc, workspace=work)
+    dq.w8a8_linear(*args, yf, workspace=work)
     torch.cuda.synchronize()
     acc_ref = oracle.int8_matmul_exact(a, b)
     assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
@@ -74,7 +78,9 @@ def test_w8a8_linear_full_shapes_sampled():
         a, b, sa, sb, bias = ditsynth.int8_operands(M, N, K, seed=N + K)
         acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
         y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-        dq.w8a8_linear(dev(a, torch.int8), dev(sa), dev(b, torch.int8), dev(sb), dev(bias), y, acc_out=acc)
+        work = torch.empty((dq.w8a8_linear_workspace_bytes(),), dtype=torch.uint8, device=DEV)
+        dq.w8a8_linear(dev(a, torch.int8), dev(sa), dev(b, torch.int8), dev(sb), dev(bias), y, acc_out=acc,
+                       workspace=work)
         torch.cuda.synchronize()
         ms = rng.integers(0, M, 256)
         ns = rng.integers(0, N, 256)
