@@ -23,7 +23,8 @@ constexpr int AQ = 128;                 // queries per workgroup
 constexpr int AK = 64;                  // keys per tile
 constexpr int KS_STRIDE = 128 * 2 + 16; // bytes per key row of the K tile (272 = 16 mod 128:
                                         // eight rows read together hit eight bank groups)
-constexpr int VT_STRIDE = AK * 2;       // bytes per d row of the transposed V tile
+constexpr int VT_STRIDE = AK * 2 + 16;  // bytes per d row of the transposed V tile (144 = 16
+                                        // mod 128, same reason)
 constexpr int KS_BYTES = AK * KS_STRIDE;
 constexpr int VT_BYTES = 128 * VT_STRIDE;
 constexpr int ABUF_BYTES = KS_BYTES + VT_BYTES;
@@ -41,10 +42,22 @@ __device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
     return e;
 }
 
-// Transposed V tile: element (d, key) lives in 8-byte slot (key/4) ^ vt_swz(d)
-// of row d.  Conflict-free for both the transposing writes (16 lanes with d
-// spaced by 8) and the MFMA operand reads (16 lanes with consecutive d).
-__device__ __forceinline__ int vt_addr(int d, int kc) { return d * VT_STRIDE + ((kc ^ ((2 * d + (d >> 3)) & 15)) << 3); }
+// Transposed V tile.  Keys are stored in the order the S^T accumulator hands
+// them to a lane for the PV product: within each 16-key block, key k sits at
+// position (k % 4) + 4*((k / 8) % 2) + 8*((k / 4) % 2), so the 8 keys one
+// lane contributes to an MFMA step are 8 consecutive positions (one 16-byte
+// read at a constant offset from a per-lane base).  With 144-byte rows the
+// operand reads (8 lanes, consecutive d) and the transposing 8-byte writes
+// (16 lanes, 16 different key groups of one d row) are both conflict-free.
+
+// Raw buffer resource over the rows [j0, T_k) of one head of K or V: rows at
+// or past T_k lie beyond num_records and read as zero.  Rebased per tile, so
+// the 32-bit offsets only span one tile.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* base, int j0, int T_k, int ld) {
+    const int64_t bytes = (int64_t)(T_k - j0 - 1) * ld * 2 + 256;
+    const int nrec = bytes <= 0 ? 0 : bytes >= 0x7fffffff ? 0x7fffffff : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)j0 * ld), 0, nrec, 0x00020000);
+}
 
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
@@ -76,20 +89,25 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
         for (int kb = 0; kb < 8; ++kb) qf[kb] = q_ok ? *reinterpret_cast<const v8bf*>(qrow + kb * 16) : v8bf{};
     }
 
-    // global -> register staging of one K/V tile: K: keys c/16 (+16 i), chunk
-    // c%16; V: keys 4*kg .. 4*kg+3, d-chunk dc.
+    // global -> register staging of one K/V tile.  K: keys kkey + 16 i, chunk
+    // kch; V: keys 4*kg .. 4*kg+3, d-chunk dc.  Keys past T_k read as zero:
+    // their scores are masked and their P is exactly 0.
     const int kkey = tid / 16, kch = tid % 16;
-    const int dc = tid % 16, kg = tid / 16;
-    const __bf16* kbase = Kg + h * 128 + kch * 8;
-    const __bf16* vbase = Vg + h * 128 + dc * 8;
+    const int kg = tid % 16, dc = tid / 16;
+    const __bf16* kbase = Kg + h * 128;
+    const __bf16* vbase = Vg + h * 128;
+    const int koff = kkey * ldk * 2 + kch * 16;
+    const int voff = kg * 4 * ldv * 2 + dc * 16;
+    // LDS position of this thread's first V key (its 4 keys are consecutive)
+    const int vpos = 16 * (kg / 4) + ((kg % 4) == 1 ? 8 : (kg % 4) == 2 ? 4 : (kg % 4) == 3 ? 12 : 0);
     v4i rk[4], rv[4];
     auto gload = [&](int j0) {
+        const __amdgpu_buffer_rsrc_t kr = kv_rsrc(kbase, j0, T_k, ldk);
+        const __amdgpu_buffer_rsrc_t vr = kv_rsrc(vbase, j0, T_k, ldv);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int gk = j0 + kkey + 16 * i;
-            rk[i] = gk < T_k ? *reinterpret_cast<const v4i*>(kbase + (size_t)gk * ldk) : v4i{0, 0, 0, 0};
-            const int gv = j0 + kg * 4 + i;
-            rv[i] = gv < T_k ? *reinterpret_cast<const v4i*>(vbase + (size_t)gv * ldv) : v4i{0, 0, 0, 0};
+            rk[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(kr, koff, i * 16 * ldk * 2, 0);
+            rv[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vr, voff, i * ldv * 2, 0);
         }
     };
     auto sstore = [&](int buf) {
@@ -99,16 +117,19 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<v4i*>(ks + (kkey + 16 * i) * KS_STRIDE + kch * 16) = rk[i];
         // transpose: 4 keys x 8 dims -> 8 rows (d) of 4 keys
+        uint8_t* vdst = vt + dc * 8 * VT_STRIDE + vpos * 2;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int w = r / 2, sh = (r % 2) * 16;
+            const int w = r / 2;
+            const uint32_t sel = (r % 2) ? 0x07060302u : 0x05040100u;
             uint2 packed;
-            packed.x = ((uint32_t)rv[0][w] >> sh & 0xFFFFu) | (((uint32_t)rv[1][w] >> sh & 0xFFFFu) << 16);
-            packed.y = ((uint32_t)rv[2][w] >> sh & 0xFFFFu) | (((uint32_t)rv[3][w] >> sh & 0xFFFFu) << 16);
-            *reinterpret_cast<uint2*>(vt + vt_addr(dc * 8 + r, kg)) = packed;
+            packed.x = __builtin_amdgcn_perm((uint32_t)rv[1][w], (uint32_t)rv[0][w], sel);
+            packed.y = __builtin_amdgcn_perm((uint32_t)rv[3][w], (uint32_t)rv[2][w], sel);
+            *reinterpret_cast<uint2*>(vdst + r * VT_STRIDE) = packed;
         }
     };
-
+    // V^T operand reads: chunk (2b + hh) of row d = dt*32 + lq
+    const int vrd = lq * VT_STRIDE + hh * 16;
     v16f oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = v16f{};
@@ -186,12 +207,8 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
         for (int b = 0; b < 4; ++b) {
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt) {
-                const int d = dt * 32 + lq;
-                const uint2 lo = *reinterpret_cast<const uint2*>(vt + vt_addr(d, 4 * b + hh));
-                const uint2 hi = *reinterpret_cast<const uint2*>(vt + vt_addr(d, 4 * b + 2 + hh));
-                v4i av = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<v8bf*>(&av), pb[b], oacc[dt],
-                                                                   0, 0, 0);
+                const v8bf av = *reinterpret_cast<const v8bf*>(vt + vrd + dt * 32 * VT_STRIDE + b * 32);
+                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[b], oacc[dt], 0, 0, 0);
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
