@@ -44,6 +44,30 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Whole-wave reductions through DPP (no LDS): pairs and quads by quad_perm,
+// rows of 16 by row rotations, then the four row results via readlane.  All
+// 64 lanes must be active; every lane gets the same (wave-uniform) result.
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+__device__ __forceinline__ float wave_allsum(float v) {
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x124>(v);   // row_ror:4
+    v += dpp_f<0x128>(v);   // row_ror:8
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_allmax(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x124>(v));
+    v = fmaxf(v, dpp_f<0x128>(v));
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
 // Block-wide reduction over `nwaves` waves through a small LDS array.
 template <int NWAVES, bool MAX>
 __device__ __forceinline__ float block_reduce(float v, float* red) {
@@ -79,12 +103,15 @@ __device__ __forceinline__ int seg_set(const SegMap& sm, int64_t row) {
 }
 
 // tanh-approximated GELU, 0.5 u (1 + tanh(k (u + 0.044715 u^3))) with
-// k = sqrt(2/pi), evaluated as u * sigmoid(2 k (u + 0.044715 u^3)) (the same
-// function: 0.5 (1 + tanh(x)) = 1 / (1 + exp(-2x))) with the hardware exp and
-// reciprocal (a few ulp in fp32, far below the bf16 rounding that follows).
+// k = sqrt(2/pi), evaluated as u / (1 + exp(-2k (u + 0.044715 u^3))) (the
+// same function: 0.5 (1 + tanh(x)) = 1 / (1 + exp(-2x))), with the constants
+// folded into one base-2 exponent and the hardware exp2 and reciprocal (a few
+// ulp in fp32, far below the bf16 rounding that follows).  Large |u| saturate
+// correctly: exp2 -> inf gives 0, exp2 -> 0 gives u.
 __device__ __forceinline__ float gelu_tanh_fast(float u) {
-    const float z = 1.5957691216057308f * u * fmaf(0.044715f * u, u, 1.0f);
-    const float e = __expf(-z);
+    constexpr float A = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    constexpr float B = A * 0.044715f;
+    const float e = __builtin_amdgcn_exp2f(u * fmaf(B, u * u, A));
     return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
@@ -95,6 +122,77 @@ __device__ __forceinline__ int8_t quant_code(float v, float s) {
     float r = rintf(__fdiv_rn(v, s));
     r = fminf(fmaxf(r, -127.0f), 127.0f);
     return (int8_t)(int)r;
+}
+
+// Hides a value from the optimizer (no instruction): later unpacking of a
+// packed row re-derives floats from it instead of keeping every float alive.
+__device__ __forceinline__ void opaque(v4i& v) { asm volatile("" : "+v"(v)); }
+
+// bf16 pair <-> two floats (low half first).
+__device__ __forceinline__ float bf_lo(int w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf_hi(int w) { return __builtin_bit_cast(float, w & (int)0xFFFF0000); }
+__device__ __forceinline__ int bf_pack(float lo, float hi) {
+    v2bf p;
+    p[0] = to_bf16(lo);
+    p[1] = to_bf16(hi);
+    return __builtin_bit_cast(int, p);
+}
+
+// Int8 codes of 8 values for scale s = fl(amax / 127) of a set containing
+// them, identical to quant_code.  With inv = fl(1/s) and s normal,
+// t = fl(v * inv) lies within 2.3e-5 of fl(v / s) and |t| < 127.00003, so
+// both round to the same integer (no clamp needed) unless t is within that
+// distance of a half-integer.  Rounding is t + 1.5*2^23, whose fp32 add rounds
+// to nearest even and leaves the integer's two's-complement low byte in the
+// low byte of the sum.  Chunks with any t closer than 1e-4 to a half-integer
+// take the IEEE division (a wave-uniform branch, rare); fast == false (s tiny
+// or zero) always divides.
+__device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float inv, bool fast) {
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    int b[8];
+    float dev = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float t = v[e] * inv;
+        const float m = t + kMagic;
+        dev = fmaxf(dev, fabsf(t - (m - kMagic)));
+        b[e] = __builtin_bit_cast(int, m);
+    }
+    if (__builtin_expect(__any(!fast || !(dev < 0.4999f)), 0)) {
+        if (!fast || !(dev < 0.4999f)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = quant_code(v[e], s);
+        }
+    }
+    // low bytes: [b0 b1 b2 b3], [b4 b5 b6 b7]
+    const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)b[1], (uint32_t)b[0], 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)b[3], (uint32_t)b[2], 0x0c0c0400u);
+    const uint32_t p45 = __builtin_amdgcn_perm((uint32_t)b[5], (uint32_t)b[4], 0x0c0c0400u);
+    const uint32_t p67 = __builtin_amdgcn_perm((uint32_t)b[7], (uint32_t)b[6], 0x0c0c0400u);
+    uint2 o;
+    o.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+    return o;
+}
+
+// Raw buffer resource over `bytes` bytes at p: loads past the end read zero,
+// stores past the end are dropped (bounds handled without branches).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return (v4i)__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(uint2 v, __amdgpu_buffer_rsrc_t r, int off) {
+    typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+    v2u d;
+    d[0] = v.x;
+    d[1] = v.y;
+    __builtin_amdgcn_raw_buffer_store_b64(d, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(v4i v, __amdgpu_buffer_rsrc_t r, int off) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    __builtin_amdgcn_raw_buffer_store_b128((v4u)v, r, off, 0, 0);
 }
 
 }  // namespace dit

@@ -57,9 +57,64 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict_
     }
 }
 
+// One wave per bf16 row (four rows per workgroup), for K <= 512 * MAXC: the
+// row stays in registers as packed bf16 pairs, reductions are DPP-only, so
+// waves never wait on each other and the whole grid is resident at once for
+// the block's widths.  Same codes and scales as quantize_rows_kernel.
+template <int MAXC, bool GELU_PRE>
+__global__ void __launch_bounds__(256) quantize_rows_wave_kernel(const __bf16* __restrict__ x, int64_t M,
+                                                                 int K, int64_t ldx, int8_t* __restrict__ q,
+                                                                 float* __restrict__ scale) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (row >= M) return;
+    const auto xr = raw_rsrc(x + row * ldx, K * 2);
+    v4i buf[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) buf[i] = buf_load16(xr, (i * kWave + lane) * 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            float lo = bf_lo(buf[i][w]), hi = bf_hi(buf[i][w]);
+            if constexpr (GELU_PRE) {
+                lo = gelu_tanh_fast(lo);
+                hi = gelu_tanh_fast(hi);
+                buf[i][w] = bf_pack(lo, hi);
+                lo = bf_lo(buf[i][w]);
+                hi = bf_hi(buf[i][w]);
+            }
+            amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
+        }
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) opaque(buf[i]);
+    amax = wave_allmax(amax);
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (lane == 0) scale[row] = s;
+    const float inv = __fdiv_rn(1.0f, s);
+    const bool fast = s >= 0x1p-100f;
+    const auto qr = raw_rsrc(q + row * K, K);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        float v[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = bf_lo(buf[i][w]);
+            v[2 * w + 1] = bf_hi(buf[i][w]);
+        }
+        buf_store8(quant8(v, s, inv, fast), qr, (i * kWave + lane) * 8);
+    }
+}
+
 hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, float* scale, hipStream_t st) {
     if (M == 0) return hipSuccess;
+    if (bf16 && K <= 4096) {
+        quantize_rows_wave_kernel<8, false><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
+            (const __bf16*)x, M, (int)K, ldx, q, scale);
+        return hipGetLastError();
+    }
     if (bf16) {
         const int nchunk = (int)(K / 8);
         if (nchunk <= 256 * 4)
@@ -83,6 +138,11 @@ hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, 
 hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
                                      hipStream_t st) {
     if (M == 0) return hipSuccess;
+    if (K <= 16384) {
+        quantize_rows_wave_kernel<32, true><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
+            (const __bf16*)u, M, (int)K, K, q, scale);
+        return hipGetLastError();
+    }
     if (K / 8 <= 256 * 4)
         quantize_rows_kernel<__bf16, 4, true><<<dim3((unsigned)M), dim3(256), 0, st>>>(
             (const __bf16*)u, K, K, q, scale);
@@ -170,10 +230,103 @@ __global__ void __launch_bounds__(256) adaln_kernel(const T* __restrict__ x, int
         }
 }
 
+// bf16 rows of width D <= 512 * MAXC, one wave per row (four per workgroup):
+// the row is held as packed bf16 pairs, mean, variance and amax are DPP wave
+// reductions, and the modulation vectors are read 16 bytes at a time.
+template <int MAXC>
+__global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restrict__ x, int64_t M, int D,
+                                                         const float* __restrict__ shift0,
+                                                         const float* __restrict__ scale0,
+                                                         int64_t mod_stride, SegMap sm, float eps,
+                                                         __bf16* __restrict__ h, int8_t* __restrict__ qo,
+                                                         float* __restrict__ qs) {
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    if (row >= M) return;
+    const int nchunk = D / 8;
+    const auto xr = raw_rsrc(x + row * D, D * 2);
+    const int set = seg_set(sm, row);
+    const float* shift = shift0 + (int64_t)set * mod_stride;
+    const float* scl = scale0 + (int64_t)set * mod_stride;
+    v4i buf[MAXC];
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) buf[i] = buf_load16(xr, (i * kWave + lane) * 16);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) s += bf_lo(buf[i][w]) + bf_hi(buf[i][w]);
+        opaque(buf[i]);
+    }
+    const float mean = wave_allsum(s) / (float)D;
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+        if (i * kWave + lane < nchunk)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float a = bf_lo(buf[i][w]) - mean, b = bf_hi(buf[i][w]) - mean;
+                ss += a * a + b * b;
+            }
+    const float var = wave_allsum(ss) / (float)D;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        const int c = i * kWave + lane;
+        if (c < nchunk) {
+            const v4f sc0 = *reinterpret_cast<const v4f*>(scl + c * 8);
+            const v4f sc1 = *reinterpret_cast<const v4f*>(scl + c * 8 + 4);
+            const v4f sh0 = *reinterpret_cast<const v4f*>(shift + c * 8);
+            const v4f sh1 = *reinterpret_cast<const v4f*>(shift + c * 8 + 4);
+            const float scv[8] = {sc0[0], sc0[1], sc0[2], sc0[3], sc1[0], sc1[1], sc1[2], sc1[3]};
+            const float shv[8] = {sh0[0], sh0[1], sh0[2], sh0[3], sh1[0], sh1[1], sh1[2], sh1[3]};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const float lo = (bf_lo(buf[i][w]) - mean) * rstd * (1.0f + scv[2 * w]) + shv[2 * w];
+                const float hi = (bf_hi(buf[i][w]) - mean) * rstd * (1.0f + scv[2 * w + 1]) + shv[2 * w + 1];
+                buf[i][w] = bf_pack(lo, hi);
+                amax = fmaxf(amax, fmaxf(fabsf(bf_lo(buf[i][w])), fabsf(bf_hi(buf[i][w]))));
+            }
+        }
+        opaque(buf[i]);
+    }
+    if (qo == nullptr) {
+        const auto hr = raw_rsrc(h + row * D, D * 2);
+#pragma unroll
+        for (int i = 0; i < MAXC; ++i) buf_store16(buf[i], hr, (i * kWave + lane) * 16);
+        return;
+    }
+    amax = wave_allmax(amax);
+    const float sq = __fdiv_rn(amax, 127.0f);
+    if (lane == 0) qs[row] = sq;
+    const float inv = __fdiv_rn(1.0f, sq);
+    const bool fast = sq >= 0x1p-100f;
+    const auto qr = raw_rsrc(qo + row * D, D);
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+        float v[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            v[2 * w] = bf_lo(buf[i][w]);
+            v[2 * w + 1] = bf_hi(buf[i][w]);
+        }
+        buf_store8(quant8(v, sq, inv, fast), qr, (i * kWave + lane) * 8);
+    }
+}
+
+static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                         const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
                         float* qs, hipStream_t st) {
     if (M == 0) return hipSuccess;
+    if (bf16 && D % 8 == 0 && D <= 4096 && mod_stride % 4 == 0 && al16(x) && al16(shift) && al16(scale) &&
+        (qo ? ((uintptr_t)qo & 7) == 0 : al16(h))) {
+        adaln_wave_kernel<8><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
+            (const __bf16*)x, M, (int)D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs);
+        return hipGetLastError();
+    }
     // D % 2048 != 0 (e.g. 512) is handled by VPT=8 with nvec = D/2048 == 0 -> use
     // the scalar-tail variant below.
     if (D % 2048 == 0) {
