@@ -15,10 +15,17 @@ HIP library through its C ABI.  Per-launch kernel times come from HIP events
 recorded by the library around each launch in the timed region.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-edit]
+  python bench.py --copy-probe MIB   # plain bf16 copy of MIB MiB, for HBM counter calibration
+
+roofline.traffic: HBM bytes per int8 GEMM launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE passes over this script, each divided by what the same counter reads
+per byte of the --copy-probe copy (profiles/gemm_w8a8_1024px_traffic.json); it
+is null when gemm.hip no longer matches the hash recorded with the counters.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -70,6 +77,36 @@ def hbm_bytes(T, D, F):
         "quant_o": T * (2 * D + D + 4),
         "quant_g": T * (2 * F + F + 4),
     }
+
+
+def gemm_traffic():
+    """Counter-derived HBM bytes per int8 GEMM launch, or None if stale/absent."""
+    path = os.path.join(ROOT, "profiles", "gemm_w8a8_1024px_traffic.json")
+    src = os.path.join(ROOT, "diffusion_transformer_text_qwen_amd", "csrc", "gemm.hip")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    if t.get("gemm_source_sha256") != sha:
+        return None
+    fetch = t["fetch_kib_per_launch"] * 1024 / t["copy_fetch_per_byte"]
+    write = t["write_kib_per_launch"] * 1024 / t["copy_write_per_byte"]
+    return int(fetch + write)
+
+
+def copy_probe(mib, dq, torch):
+    """dit_cast bf16 -> bf16 over mib MiB: reads and writes exactly 2n bytes."""
+    n = mib * (1 << 20) // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(5):
+        dq.cast(x, y)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe": {"dispatches": 5, "bytes_read_per_dispatch": 2 * n,
+                                     "bytes_written_per_dispatch": 2 * n}}), flush=True)
 
 
 def site_report(prof, per_block_ops, n_blocks_timed, peak, unit):
@@ -249,6 +286,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-edit", action="store_true")
     ap.add_argument("--edit-reps", type=int, default=5)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -261,6 +299,9 @@ def main():
 
     dq.lib()
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, dq, torch)
+        return
     w, ms, prof, ok = run_stack(args, dq, torch, ditsynth)
     T, D, F = w.T, w.D, w.F
     n_timed = args.steps * w.n_blocks
@@ -296,8 +337,9 @@ def main():
                    "blocks": w.n_blocks, "tokens": T, "image_tokens": w.seg_len[-1], "hidden": D,
                    "heads": w.H, "mlp": F, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
-                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": None,
-                     "kernel": "gemm_mfma_kernel<int8> (W8A8 linears, 4 launches per block)",
+                     "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": gemm_traffic(),
+                     "kernel": "gemm_large_kernel<int8> (+ K-split tail and its reduce): the four W8A8 "
+                               "linears of a block, one launch site each",
                      "algorithmic_ops_per_launch": int(avg_launch_ops),
                      "avg_launch_us": round(avg_launch_s * 1e6, 2)},
         "kernels": kernels,
