@@ -27,7 +27,6 @@ constexpr int VT_STRIDE = AK * 2 + 16;  // bytes per d row of the transposed V t
                                         // mod 128, same reason)
 constexpr int KS_BYTES = AK * KS_STRIDE;
 constexpr int VT_BYTES = 128 * VT_STRIDE;
-constexpr int ABUF_BYTES = KS_BYTES + VT_BYTES;
 // Rescale threshold of the online softmax, in log2 units: the running max is
 // only raised when a tile's max exceeds it by more than this, so P <= 2^8.
 constexpr float kRescaleLog2 = 8.0f;
@@ -59,11 +58,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* base, in
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)j0 * ld), 0, nrec, 0x00020000);
 }
 
+// Software pipeline over key tiles.  K and V have separate double buffers, K
+// one tile ahead: while the VALU turns the scores of tile t into P, the MFMA
+// pipe computes the scores of tile t+1; then P V of tile t runs while tile
+// t+2's K and tile t+1's V go from registers to LDS and the global loads of
+// the next ones are issued.  One barrier per tile.
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                  const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int T_q, int T_k,
                  int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * ABUF_BYTES];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KS_BYTES + 2 * VT_BYTES];
+    uint8_t* const kbuf0 = lds;
+    uint8_t* const kbuf1 = lds + KS_BYTES;
+    uint8_t* const vbuf0 = lds + 2 * KS_BYTES;
+    uint8_t* const vbuf1 = lds + 2 * KS_BYTES + VT_BYTES;
 
     const int nqb = (T_q + AQ - 1) / AQ;
     const int qb = nqb - 1 - (int)blockIdx.x;   // longest key ranges first
@@ -89,9 +97,9 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
         for (int kb = 0; kb < 8; ++kb) qf[kb] = q_ok ? *reinterpret_cast<const v8bf*>(qrow + kb * 16) : v8bf{};
     }
 
-    // global -> register staging of one K/V tile.  K: keys kkey + 16 i, chunk
-    // kch; V: keys 4*kg .. 4*kg+3, d-chunk dc.  Keys past T_k read as zero:
-    // their scores are masked and their P is exactly 0.
+    // global -> register staging.  K: keys kkey + 16 i, chunk kch; V: keys
+    // 4*kg .. 4*kg+3, d-chunk dc.  Keys past T_k read as zero: their scores
+    // are masked and their P is exactly 0.
     const int kkey = tid / 16, kch = tid % 16;
     const int kg = tid % 16, dc = tid / 16;
     const __bf16* kbase = Kg + h * 128;
@@ -101,21 +109,22 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
     // LDS position of this thread's first V key (its 4 keys are consecutive)
     const int vpos = 16 * (kg / 4) + ((kg % 4) == 1 ? 8 : (kg % 4) == 2 ? 4 : (kg % 4) == 3 ? 12 : 0);
     v4i rk[4], rv[4];
-    auto gload = [&](int j0) {
-        const __amdgpu_buffer_rsrc_t kr = kv_rsrc(kbase, j0, T_k, ldk);
-        const __amdgpu_buffer_rsrc_t vr = kv_rsrc(vbase, j0, T_k, ldv);
+    auto gload_k = [&](int j0) {
+        const __amdgpu_buffer_rsrc_t r = kv_rsrc(kbase, j0, T_k, ldk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            rk[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(kr, koff, i * 16 * ldk * 2, 0);
-            rv[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vr, voff, i * ldv * 2, 0);
-        }
+        for (int i = 0; i < 4; ++i) rk[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(r, koff, i * 16 * ldk * 2, 0);
     };
-    auto sstore = [&](int buf) {
-        uint8_t* ks = lds + buf * ABUF_BYTES;
-        uint8_t* vt = ks + KS_BYTES;
+    auto gload_v = [&](int j0) {
+        const __amdgpu_buffer_rsrc_t r = kv_rsrc(vbase, j0, T_k, ldv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rv[i] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(r, voff, i * ldv * 2, 0);
+    };
+    auto sstore_k = [&](uint8_t* ks) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             *reinterpret_cast<v4i*>(ks + (kkey + 16 * i) * KS_STRIDE + kch * 16) = rk[i];
+    };
+    auto sstore_v = [&](uint8_t* vt) {
         // transpose: 4 keys x 8 dims -> 8 rows (d) of 4 keys
         uint8_t* vdst = vt + dc * 8 * VT_STRIDE + vpos * 2;
 #pragma unroll
@@ -128,39 +137,34 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
             *reinterpret_cast<uint2*>(vdst + r * VT_STRIDE) = packed;
         }
     };
-    // V^T operand reads: chunk (2b + hh) of row d = dt*32 + lq
-    const int vrd = lq * VT_STRIDE + hh * 16;
-    v16f oacc[4];
+    // S^T = K Q^T for one tile: two 32-key halves
+    auto scores = [&](const uint8_t* ks, v16f(&sacc)[2]) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] = v16f{};
-    float m_run = -INFINITY, l_run = 0.0f;
-
-    const int ntiles = (kv_hi + AK - 1) / AK;
-    gload(0);
-    sstore(0);
-    if (ntiles > 1) gload(AK);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        const int j0 = t * AK;
-        const uint8_t* ks = lds + (t & 1) * ABUF_BYTES;
-        const uint8_t* vt = ks + KS_BYTES;
-
-        // S^T = K Q^T : two 32-key halves
-        v16f sacc[2];
+        for (int kh = 0; kh < 2; ++kh) sacc[kh] = v16f{};
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-            sacc[kh] = v16f{};
+        for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb) {
+            for (int kh = 0; kh < 2; ++kh) {
                 const v8bf a = *reinterpret_cast<const v8bf*>(ks + (kh * 32 + lq) * KS_STRIDE + kb * 32 + hh * 16);
                 sacc[kh] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kb], sacc[kh], 0, 0, 0);
             }
-        }
-        // stage the next tile while this one is consumed
-        if (t + 1 < ntiles) {
-            sstore((t + 1) & 1);
-            if (t + 2 < ntiles) gload(j0 + 2 * AK);
-        }
+    };
+    // V^T operand reads: chunk (2b + hh) of row d = dt*32 + lq
+    const int vrd = lq * VT_STRIDE + hh * 16;
+
+    v16f oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = v16f{};
+    const v2bf kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float m_run = -INFINITY, l_run = 0.0f;
+
+    // One pipeline step: softmax of tile t (scores in scur) overlapped with
+    // the scores of tile t+1 (into snxt, from knext); then P V of tile t from
+    // vcur; stores K(t+2) into kfree and V(t+1) into vnext; loads K(t+3),
+    // V(t+2).  Buffers past the last tile hold zeros or unused keys.
+    auto step = [&](int t, v16f(&scur)[2], v16f(&snxt)[2], const uint8_t* knext, const uint8_t* vcur,
+                    uint8_t* kfree, uint8_t* vnext) {
+        const int j0 = t * AK;
         // mask keys beyond this query's visible prefix (only tiles that cross it)
         if (j0 + AK > kv_min) {
 #pragma unroll
@@ -168,14 +172,14 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int key = j0 + kh * 32 + (j / 4) * 8 + hh * 4 + (j % 4);
-                    if (key >= my_end) sacc[kh][j] = -INFINITY;
+                    if (key >= my_end) scur[kh][j] = -INFINITY;
                 }
         }
         float mx = -INFINITY;
 #pragma unroll
         for (int kh = 0; kh < 2; ++kh)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, sacc[kh][j]);
+            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kh][j]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
         // lazy rescale: raise the running max only when this tile exceeds it by
         // more than 2^kRescaleLog2 (wave-uniform decision)
@@ -190,30 +194,97 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
             m_run = m_new;
         }
         const float mb = m_run * c_log2;
+        // Scores of tile t+1 interleaved with P of tile t: MFMA i (key half
+        // i % 2, k-block i / 2) with its operand read four ahead and P of two
+        // scores; sched_barrier keeps each group where it is written.
+        auto kfrag = [&](int i) {
+            return *reinterpret_cast<const v8bf*>(knext + ((i % 2) * 32 + lq) * KS_STRIDE + (i / 2) * 32 + hh * 16);
+        };
+        v8bf kf[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
+        snxt[0] = v16f{};
+        snxt[1] = v16f{};
         float psum = 0.0f;
         v8bf pb[4];
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kh][j], c_log2, -mb));
-                psum += p;
-                pb[kh * 2 + j / 8][j % 8] = to_bf16(p);
+        for (int i = 0; i < 16; ++i) {
+            if (i + 4 < 16) kf[i + 4] = kfrag(i + 4);
+            snxt[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i / 2], snxt[i % 2], 0, 0, 0);
+            {
+                // P of scores 2i, 2i+1 (bf16, as the PV MFMA takes them); the
+                // row sum adds the same rounded values with one dot2
+                const int e = 2 * i;
+                v2bf p2;
+                p2[0] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16], c_log2, -mb)));
+                p2[1] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16 + 1], c_log2, -mb)));
+                pb[e / 8][e % 8] = p2[0];
+                pb[e / 8][e % 8 + 1] = p2[1];
+                psum = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, psum, false);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         l_run += psum;
-
-        // O^T += V^T P^T, 16 keys per MFMA in the S^T lane order
+        // O^T += V^T P^T (16 keys per MFMA in the S^T lane order; MFMA i: key
+        // block i / 4, d tile i % 4), operands read four ahead; the LDS stores
+        // of K(t+2) and V(t+1) and the loads of K(t+3), V(t+2) in between.
+        auto vfrag = [&](int i) {
+            return *reinterpret_cast<const v8bf*>(vcur + vrd + (i % 4) * 32 * VT_STRIDE + (i / 4) * 32);
+        };
+        v8bf vf[16];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int i = 0; i < 4; ++i) vf[i] = vfrag(i);
+        const __amdgpu_buffer_rsrc_t krs = kv_rsrc(kbase, j0 + 3 * AK, T_k, ldk);
+        const __amdgpu_buffer_rsrc_t vrs = kv_rsrc(vbase, j0 + 2 * AK, T_k, ldv);
+        uint8_t* vdst = vnext + dc * 8 * VT_STRIDE + vpos * 2;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const v8bf av = *reinterpret_cast<const v8bf*>(vt + vrd + dt * 32 * VT_STRIDE + b * 32);
-                oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[b], oacc[dt], 0, 0, 0);
+        for (int i = 0; i < 16; ++i) {
+            if (i + 4 < 16) vf[i + 4] = vfrag(i + 4);
+            oacc[i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb[i / 4], oacc[i % 4], 0, 0, 0);
+            if (i < 4) {
+                *reinterpret_cast<v4i*>(kfree + (kkey + 16 * i) * KS_STRIDE + kch * 16) = rk[i];
+            } else if (i < 12) {
+                // transpose: 4 keys x 8 dims -> row d = dc*8 + r of 4 keys
+                const int r = i - 4, w = r / 2;
+                const uint32_t sel = (r % 2) ? 0x07060302u : 0x05040100u;
+                uint2 packed;
+                packed.x = __builtin_amdgcn_perm((uint32_t)rv[1][w], (uint32_t)rv[0][w], sel);
+                packed.y = __builtin_amdgcn_perm((uint32_t)rv[3][w], (uint32_t)rv[2][w], sel);
+                *reinterpret_cast<uint2*>(vdst + r * VT_STRIDE) = packed;
+            } else if (i < 14) {
+#pragma unroll
+                for (int q = 2 * (i - 12); q < 2 * (i - 12) + 2; ++q)
+                    rk[q] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(krs, koff, q * 16 * ldk * 2, 0);
+            } else {
+#pragma unroll
+                for (int q = 2 * (i - 14); q < 2 * (i - 14) + 2; ++q)
+                    rv[q] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vrs, voff, q * ldv * 2, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
+    };
+
+    const int ntiles = (kv_hi + AK - 1) / AK;
+    // prologue: K(0), V(0), K(1) in LDS; K(2), V(1) in registers; scores of tile 0
+    gload_k(0);
+    gload_v(0);
+    sstore_k(kbuf0);
+    sstore_v(vbuf0);
+    gload_k(AK);
+    sstore_k(kbuf1);
+    gload_k(2 * AK);
+    gload_v(AK);
+    __syncthreads();
+    v16f sa[2], sb[2];
+    scores(kbuf0, sa);
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(t, sa, sb, kbuf1, vbuf0, kbuf0, vbuf1);
+        step(t + 1, sb, sa, kbuf0, vbuf1, kbuf1, vbuf0);
     }
+    if (t < ntiles) step(t, sa, sb, kbuf1, vbuf0, kbuf0, vbuf1);
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
     if (!q_ok) return;
