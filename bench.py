@@ -6,13 +6,19 @@ MLP 16384) plus the DiT head (img_in, txt_in), tail (final adaLN, proj_out) and
 the FlowMatch Euler update of the 4096 x 64 latent.  Reported value: DiT-block
 tokens/s = 32 * 4352 block rows / step time.
 
+Also measured (reported under "denoise_loop_1024px"): the whole 40-step loop of
+the same generation, eager and with one DiT evaluation captured in a HIP graph
+and replayed (Euler updates between replays).
+
 Also measured (reported under "edit_2048px"): one block of the 2048x2048 edit
 workload, [256 text | 1024 reference | 16384 target], uncached step (17,664
 rows) and the cached step that reuses the prefix K/V (16,384 rows).
 
 Inputs are seeded synthetic tensors (ditsynth); the path runs entirely in the
-HIP library through its C ABI.  Per-launch kernel times come from HIP events
-recorded by the library around each launch in the timed region.
+HIP library through its C ABI.  value / ms_per_step come from K timed steps
+without instrumentation; per-launch kernel times (roofline, kernels) from HIP
+events the library records around each launch during K more timed steps
+(ms_per_step_profiled: their step time).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-edit]
   python bench.py --copy-probe MIB   # plain bf16 copy of MIB MiB, for HBM counter calibration
@@ -149,37 +155,26 @@ def run_stack(args, dq, torch, ditsynth):
     cos = torch.empty((T, 64), dtype=torch.float32, device=dev)
     sin = torch.empty((T, 64), dtype=torch.float32, device=dev)
     dq.rope_tables(L, w.images, 0, T, cos, sin)
-    kc = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(w.n_blocks)]
-    vc = [torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev) for _ in range(w.n_blocks)]
-    ws = torch.empty(dq.workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
-    x = torch.empty((T, D), dtype=torch.bfloat16, device=dev)
-    lat = si["latent"].clone()
-    lat_b = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
+    from diffusion_transformer_text_qwen_amd.loop import DenoiseLoop
+    head = dq.HeadWeights({"w_txt_in": si["w_txt_in"].to(torch.bfloat16), "b_txt_in": si["b_txt_in"],
+                           "w_img_in": si["w_img_in"].to(torch.bfloat16), "b_img_in": si["b_img_in"],
+                           "w_proj_out": si["w_proj_out"].to(torch.bfloat16), "b_proj_out": si["b_proj_out"]})
     txt_b = si["txt_feats"].to(torch.bfloat16)
-    w_txt = si["w_txt_in"].to(torch.bfloat16)
-    w_img = si["w_img_in"].to(torch.bfloat16)
-    w_out = si["w_proj_out"].to(torch.bfloat16)
-    mod = si["mod"][0:1].contiguous()
-    mf = si["mod_final"][0]
-    hf = torch.empty((N, D), dtype=torch.bfloat16, device=dev)
-    vel = torch.empty((N, 64), dtype=torch.bfloat16, device=dev)
-    mos = [0] * len(w.seg_len)
+    loop = DenoiseLoop(cfg, blocks, head, w.seg_len, [0] * len(w.seg_len), L, cos, sin, n_mod=1)
+    loop.mod.copy_(si["mod"][0:1])
+    loop.mod_final.copy_(si["mod_final"][0])
+    lat = si["latent"].clone()
     sigma, sigma_next = 1.0, 1.0 - 0.98 / 39.0
 
     def step():
-        dq.cast(lat, lat_b)
-        dq.bf16_linear(txt_b, w_txt, si["b_txt_in"], x[:L])
-        dq.bf16_linear(lat_b, w_img, si["b_img_in"], x[L:])
-        dq.stack_forward(cfg, blocks, x, mod, mos, cos, sin, w.seg_len, kc, vc, ws)
-        dq.adaln_modulate(x[L:], mf[0], mf[1], h_out=hf)
-        dq.bf16_linear(hf, w_out, si["b_proj_out"], vel)
-        dq.euler_step(lat, vel, sigma, sigma_next)
+        loop.velocity(lat, txt_b)
+        dq.euler_step(lat, loop.vel, sigma, sigma_next)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ok = bool(torch.isfinite(x.float()).all().item()) and bool(torch.isfinite(lat).all().item())
-    dq.profile_begin(args.steps * w.n_blocks * 10 + 16)
+    ok = bool(torch.isfinite(loop.vel.float()).all().item()) and bool(torch.isfinite(lat).all().item())
+    # timed steps (no per-kernel events: they add ~4% per step)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     ev0.record()
@@ -187,9 +182,46 @@ def run_stack(args, dq, torch, ditsynth):
         step()
     ev1.record()
     torch.cuda.synchronize()
-    prof = dq.profile_end()
     ms = ev0.elapsed_time(ev1) / args.steps
-    return w, ms, prof, ok
+    # the same steps again with HIP events around every launch (per-kernel times)
+    dq.profile_begin(args.steps * w.n_blocks * 10 + 16)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    prof = dq.profile_end()
+    ms_prof = ev0.elapsed_time(ev1) / args.steps
+    res_loop = None
+    if args.loop_steps:
+        res_loop = run_loop(args, torch, ditsynth, w, loop, si["latent"], txt_b, None)
+    return w, ms, ms_prof, prof, ok, res_loop
+
+
+def run_loop(args, torch, ditsynth, w, loop, latent0, txt, ref):
+    """The whole denoise loop (args.loop_steps steps of the 40-step schedule),
+    eager and with one velocity evaluation captured in a HIP graph and replayed."""
+    steps = args.loop_steps
+    li = ditsynth.device_loop_inputs(w, steps)
+    cache = len(w.images) > 1
+    res = {"steps": steps, "prefix_cached": cache}
+    for label, graph in (("eager", False), ("graph", True)):
+        lat = latent0.clone()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        loop.run(lat, txt, ref, li["mods"], li["mod_finals"], li["sigmas"], cache_prefix=cache, graph=graph)
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{label}_ms"] = round(e0.elapsed_time(e1), 2)
+        res[f"{label}_finite"] = bool(torch.isfinite(lat).all().item())
+    rows = w.T + (steps - 1) * (w.seg_len[-1] if cache else w.T)
+    best = min(res["graph_ms"], res["eager_ms"])
+    res["block_tokens_per_s"] = round(w.n_blocks * rows / (best * 1e-3), 1)
+    res["ms_per_step"] = round(best / steps, 3)
+    log(f"loop: {res}")
+    return res
 
 
 def run_edit(args, dq, torch, ditsynth, reps):
@@ -287,6 +319,8 @@ def main():
     ap.add_argument("--no-edit", action="store_true")
     ap.add_argument("--edit-reps", type=int, default=5)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--loop-steps", type=int, default=40,
+                    help="steps of the timed denoise loop after the step benchmark (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -302,7 +336,7 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe, dq, torch)
         return
-    w, ms, prof, ok = run_stack(args, dq, torch, ditsynth)
+    w, ms, ms_prof, prof, ok, loop = run_stack(args, dq, torch, ditsynth)
     T, D, F = w.T, w.D, w.F
     n_timed = args.steps * w.n_blocks
     value = w.n_blocks * T / (ms * 1e-3)
@@ -327,6 +361,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 3),
+        "ms_per_step_profiled": round(ms_prof, 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -346,6 +381,8 @@ def main():
         "block_ms_sum_of_launches": round(block_ms, 4),
         "finite": ok,
     }
+    if loop is not None:
+        line["denoise_loop_1024px"] = loop
     if not args.no_edit:
         line["edit_2048px"] = run_edit(args, dq, torch, ditsynth, args.edit_reps)
     if not args.no_cpu_baseline:

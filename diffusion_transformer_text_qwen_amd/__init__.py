@@ -48,6 +48,18 @@ class BlockIO(ctypes.Structure):
                 ("k_cache", _vp), ("v_cache", _vp)]
 
 
+class HeadWeightsC(ctypes.Structure):
+    _fields_ = [("w_txt_in", _vp), ("b_txt_in", _vp), ("w_img_in", _vp), ("b_img_in", _vp),
+                ("w_proj_out", _vp), ("b_proj_out", _vp), ("C_txt", _c_i32), ("C_lat", _c_i32)]
+
+
+class VelocityIO(ctypes.Structure):
+    _fields_ = [("txt_feats", _vp), ("ref_latent", _vp), ("latent", _vp), ("L_txt", _c_i64), ("R", _c_i64),
+                ("N", _c_i64), ("mod", _vp), ("n_mod", _c_i32), ("mod_of_seg", _vp), ("mod_final", _vp),
+                ("cos_t", _vp), ("sin_t", _vp), ("seg_len", _vp), ("n_seg", _c_i32), ("T_q", _c_i64),
+                ("k_caches", _vp), ("v_caches", _vp), ("vel", _vp)]
+
+
 _SIGS = {
     "dit_abi_version": ([], ctypes.c_int),
     "dit_status_string": ([ctypes.c_int], ctypes.c_char_p),
@@ -76,6 +88,10 @@ _SIGS = {
                            _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "dit_stack_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), _c_i32,
                            ctypes.POINTER(BlockIO), _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "dit_velocity_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64, _c_i32], ctypes.c_size_t),
+    "dit_velocity_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), _c_i32,
+                              ctypes.POINTER(HeadWeightsC), ctypes.POINTER(VelocityIO), _vp, ctypes.c_size_t,
+                              _vp], ctypes.c_int),
 }
 
 _lib = None
@@ -299,3 +315,46 @@ def stack_forward(cfg: BlockConfig, ws: Sequence[BlockWeights], x, mod, mod_of_s
                                    workspace.numel() * workspace.element_size(), _stream(stream)),
            "dit_stack_forward")
     del keep
+
+
+class HeadWeights:
+    """Device tensors of the DiT head/tail (dit_head_weights): w_txt_in [D, C_txt],
+    w_img_in [D, C_lat], w_proj_out [C_lat, D] in the activation dtype and fp32
+    biases b_txt_in, b_img_in, b_proj_out."""
+
+    def __init__(self, t: dict):
+        self.t = t
+        self.c = HeadWeightsC(
+            w_txt_in=_p(t.get("w_txt_in")), b_txt_in=_p(t.get("b_txt_in")), w_img_in=_p(t["w_img_in"]),
+            b_img_in=_p(t.get("b_img_in")), w_proj_out=_p(t["w_proj_out"]), b_proj_out=_p(t.get("b_proj_out")),
+            C_txt=t["w_txt_in"].shape[1] if t.get("w_txt_in") is not None else 0, C_lat=t["w_img_in"].shape[1])
+
+
+def velocity_workspace_bytes(cfg: BlockConfig, T_q: int, N: int, C_lat: int) -> int:
+    return int(lib().dit_velocity_workspace_bytes(ctypes.byref(cfg), T_q, N, C_lat))
+
+
+def velocity_forward(cfg: BlockConfig, ws: Sequence[BlockWeights], head: HeadWeights, latent, vel, mod,
+                     mod_of_seg, mod_final, cos_t, sin_t, seg_len, k_caches, v_caches, workspace,
+                     txt_feats=None, ref_latent=None, L_txt: int = 0, R: int = 0, T_q: Optional[int] = None,
+                     stream=None) -> None:
+    """dit_velocity_forward: vel [N, C_lat] from the target latent [N, C_lat] (fp32);
+    T_q = L_txt + R + N computes every row, T_q = N only the target rows."""
+    N = latent.shape[0]
+    T_k = int(sum(seg_len))
+    if T_q is None:
+        T_q = T_k
+    n = len(ws)
+    arr = (BlockWeightsC * max(n, 1))(*[w.c for w in ws])
+    kc = (_vp * max(n, 1))(*[_p(t) for t in k_caches])
+    vc = (_vp * max(n, 1))(*[_p(t) for t in v_caches])
+    mos = _host_i32(mod_of_seg)
+    segs = _host_i32(seg_len)
+    io = VelocityIO(txt_feats=_p(txt_feats), ref_latent=_p(ref_latent), latent=_p(latent), L_txt=L_txt, R=R, N=N,
+                    mod=_p(mod), n_mod=mod.shape[0], mod_of_seg=ctypes.cast(mos, _vp), mod_final=_p(mod_final),
+                    cos_t=_p(cos_t), sin_t=_p(sin_t), seg_len=ctypes.cast(segs, _vp), n_seg=len(seg_len), T_q=T_q,
+                    k_caches=ctypes.cast(kc, _vp), v_caches=ctypes.cast(vc, _vp), vel=_p(vel))
+    _check(lib().dit_velocity_forward(ctypes.byref(cfg), arr, n, ctypes.byref(head.c), ctypes.byref(io),
+                                      _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dit_velocity_forward")
+    del mos, segs, kc, vc, arr

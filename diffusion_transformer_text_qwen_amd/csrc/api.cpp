@@ -590,6 +590,114 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
     return DIT_OK;
 }
 
+size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t N, int32_t C_lat) {
+    if (!cfg || T_q < 0 || N < 0 || C_lat < 0) return 0;
+    const size_t es = cfg->mode == DIT_MODE_F32 ? 4 : 2;
+    return up256((size_t)T_q * cfg->D * es) + up256((size_t)T_q * C_lat * es) + up256((size_t)N * cfg->D * es) +
+           plan(cfg, T_q).total;
+}
+
+int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* blocks, int32_t n_blocks,
+                         const dit_head_weights* head, const dit_velocity_io* io, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+    int s = check_cfg(cfg);
+    if (s) return s;
+    CHECK(head != nullptr && io != nullptr, DIT_E_NULL, "head and io must be non-NULL");
+    CHECK(n_blocks >= 0 && (n_blocks == 0 || blocks != nullptr), DIT_E_NULL, "blocks is NULL");
+    CHECK(head->w_img_in && head->w_proj_out, DIT_E_NULL, "w_img_in and w_proj_out must be non-NULL");
+    CHECK(head->C_lat >= 64 && head->C_lat % 64 == 0, DIT_E_UNSUPPORTED, "C_lat must be a positive multiple of 64");
+    CHECK(io->L_txt >= 0 && io->R >= 0 && io->N >= 1, DIT_E_SHAPE, "need L_txt >= 0, R >= 0, N >= 1");
+    const int64_t T_k = io->L_txt + io->R + io->N;
+    CHECK(io->T_q == T_k || io->T_q == io->N, DIT_E_SHAPE, "T_q must be L_txt + R + N or N");
+    const bool full = io->T_q == T_k;
+    if (full && io->L_txt > 0) {
+        CHECK(head->w_txt_in && io->txt_feats, DIT_E_NULL, "text rows need w_txt_in and txt_feats");
+        CHECK(head->C_txt >= 64 && head->C_txt % 64 == 0, DIT_E_UNSUPPORTED, "C_txt must be a positive multiple of 64");
+        CHECK(aligned16(io->txt_feats) && aligned16(head->w_txt_in), DIT_E_ALIGN, "txt_feats/w_txt_in misaligned");
+    }
+    if (full && io->R > 0) CHECK(io->ref_latent != nullptr, DIT_E_NULL, "reference rows need ref_latent");
+    CHECK(io->latent && io->vel && io->mod_final, DIT_E_NULL, "latent, vel and mod_final must be non-NULL");
+    CHECK(aligned16(io->latent) && aligned16(io->vel) && (!io->ref_latent || aligned16(io->ref_latent)) &&
+              aligned16(head->w_img_in) && aligned16(head->w_proj_out) && aligned16(io->mod_final),
+          DIT_E_ALIGN, "latents, vel, head weights and mod_final must be 16-byte aligned");
+    CHECK(io->k_caches && io->v_caches, DIT_E_NULL, "cache arrays are NULL");
+    dit_block_io bio{};
+    bio.mod = io->mod;
+    bio.n_mod = io->n_mod;
+    bio.mod_of_seg = io->mod_of_seg;
+    bio.cos_t = io->cos_t;
+    bio.sin_t = io->sin_t;
+    bio.seg_len = io->seg_len;
+    bio.n_seg = io->n_seg;
+    bio.T_q = io->T_q;
+    bio.T_k = T_k;
+    for (int b = 0; b < n_blocks; ++b) {
+        s = check_weights(cfg, &blocks[b]);
+        if (s) return s;
+        CHECK(io->k_caches[b] && io->v_caches[b], DIT_E_NULL, "cache of block %d is NULL", b);
+        CHECK(aligned16(io->k_caches[b]) && aligned16(io->v_caches[b]), DIT_E_ALIGN, "caches must be 16-byte aligned");
+    }
+    const size_t need = dit_velocity_workspace_bytes(cfg, io->T_q, io->N, head->C_lat);
+    CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
+    CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
+    uint8_t* ws = (uint8_t*)workspace;
+    const int64_t D = cfg->D, C = head->C_lat, T_q = io->T_q, N = io->N;
+    const bool f32 = cfg->mode == DIT_MODE_F32;
+    const size_t es = f32 ? 4 : 2;
+    uint8_t* x = ws;
+    uint8_t* latc = x + up256((size_t)T_q * D * es);
+    uint8_t* hf = latc + up256((size_t)T_q * C * es);
+    uint8_t* blk = hf + up256((size_t)N * D * es);
+    bio.x = x;
+    bio.k_cache = n_blocks ? io->k_caches[0] : latc;   // checked below only when blocks run
+    bio.v_cache = n_blocks ? io->v_caches[0] : latc;
+    s = check_io(cfg, &bio);
+    if (s) return s;
+    hipStream_t st = S(stream);
+    // y[M, Nn] = a[M, K] w[Nn, K]^T + b in the activation dtype
+    auto linear = [&](const void* a, int64_t M, int64_t K, const void* w, const float* b, void* y,
+                      int64_t Nn) -> hipError_t {
+        if (M == 0) return hipSuccess;
+        EpiParams ep = store_epi(y, Nn, !f32, b);
+        return f32 ? launch_gemm_f32((const float*)a, K, (const float*)w, M, Nn, K, ep, st)
+                   : launch_gemm_bf16(a, K, w, M, Nn, K, ep, st);
+    };
+    // latent rows -> activation dtype (the fp32 mode reads the fp32 latent directly)
+    auto lat_rows = [&](const float* src, int64_t rows, uint8_t* dst) -> const void* {
+        if (f32) return src;
+        (void)launch_cast(src, false, dst, true, rows * C, st);
+        return dst;
+    };
+    const int64_t tgt = T_q - N;   // first target row among the computed rows
+    if (full) {
+        if (io->L_txt > 0)
+            RUN(linear(io->txt_feats, io->L_txt, head->C_txt, head->w_txt_in, head->b_txt_in, x, D), "txt_in");
+        if (io->R > 0) {
+            const void* a = lat_rows(io->ref_latent, io->R, latc);
+            RUN(hipGetLastError(), "cast ref_latent");
+            RUN(linear(a, io->R, C, head->w_img_in, head->b_img_in, x + (size_t)io->L_txt * D * es, D), "img_in ref");
+        }
+    }
+    {
+        const void* a = lat_rows(io->latent, N, latc + (size_t)(full ? io->R : 0) * C * es);
+        RUN(hipGetLastError(), "cast latent");
+        RUN(linear(a, N, C, head->w_img_in, head->b_img_in, x + (size_t)tgt * D * es, D), "img_in");
+    }
+    for (int b = 0; b < n_blocks; ++b) {
+        s = block_impl(cfg, &blocks[b], &bio, io->k_caches[b], io->v_caches[b], blk, st);
+        if (s) return s;
+    }
+    SegMap sm{};
+    sm.end[0] = N;
+    sm.set[0] = 0;
+    sm.n = 1;
+    RUN(launch_adaln(x + (size_t)tgt * D * es, !f32, N, D, io->mod_final, io->mod_final + D, 0, sm, cfg->ln_eps,
+                     hf, nullptr, nullptr, st),
+        "final adaln");
+    RUN(linear(hf, N, D, head->w_proj_out, head->b_proj_out, io->vel, C), "proj_out");
+    return DIT_OK;
+}
+
 int dit_profile_begin(int32_t capacity) {
     CHECK(!g_prof.on, DIT_E_UNSUPPORTED, "profiling already active");
     CHECK(capacity >= 1 && capacity <= (1 << 20), DIT_E_SHAPE, "capacity outside [1, 2^20]");

@@ -215,6 +215,51 @@ def step_inputs(w: Workload) -> Dict[str, np.ndarray]:
     return out
 
 
+def loop_sigmas(steps: int, total: int = 40) -> np.ndarray:
+    """Sigmas of the first ``steps`` Euler steps of a ``total``-step loop: the
+    linear schedule 1 -> 0.02 over ``total`` values, then 0 (fp32 values, so
+    both sides take the same numbers)."""
+    sched = [1.0 - 0.98 * i / (total - 1) for i in range(total)] + [0.0]
+    return np.asarray(sched[:steps + 1], dtype=np.float32)
+
+
+def loop_inputs(w: Workload, steps: int) -> Dict[str, np.ndarray]:
+    """Inputs of a ``steps``-step denoise loop: step_inputs (target latent, text
+    features, head/tail weights) plus reference latents [R, 64] for every image
+    segment but the last (editing), the modulation of each step mods
+    [S, n_mod, 6, D] with mod_of_seg, the tail modulation of each step
+    mod_finals [S, 2, D], and sigmas [S + 1].
+
+    One image segment (text-to-image): one modulation set per step for every
+    token, from that step's timestep embedding.  Several (editing): set 0 is the
+    prefix set (text and references, the same at every step), set 1 the
+    target's set of the step (the same sets as block_inputs(w, step))."""
+    si = step_inputs(w)
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 2000]))
+    D = w.D
+    R = int(sum(h * ww for h, ww in w.images[:-1]))
+    edit = len(w.images) > 1
+    out = dict(si)
+    out["ref_latent"] = _normal(rng, (R, 64)) if R else np.zeros((0, 64), np.float32)
+    if edit:
+        sets = _modulation_sets(w, 1 + steps)
+        out["mods"] = np.stack([sets[[0, 1 + i]] for i in range(steps)])
+        out["mod_of_seg"] = np.asarray([0] * (len(w.seg_len) - 1) + [1], np.int32)
+    else:
+        out["mods"] = _modulation_sets(w, steps)[:, None]
+        out["mod_of_seg"] = np.zeros(len(w.seg_len), np.int32)
+    w_mf = _normal(rng, (2 * D, D), 0.02).astype(np.float64)
+    b_mf = _normal(rng, (2 * D,), 0.02).astype(np.float64)
+    finals = []
+    for _ in range(steps):
+        temb = _normal(rng, (D,), 1.0).astype(np.float64)
+        finals.append((w_mf @ (temb / (1.0 + np.exp(-temb))) + b_mf).reshape(2, D))
+    out["mod_finals"] = np.stack(finals).astype(np.float32)
+    out["sigmas"] = loop_sigmas(steps)
+    out["seg_len"] = np.asarray(w.seg_len, np.int32)
+    return out
+
+
 def attention_inputs(T_q: int, T_k: int, H: int, seed: int, bf16: bool = True):
     """q [T_q,H,128], k/v [T_k,H,128] N(0,1) draws for attention-only cases."""
     rng = np.random.default_rng(seed)
@@ -312,4 +357,32 @@ def device_step_inputs(w: Workload, device="cuda"):
         del w_mod
     out["x_target"] = [device_normal((N, D), 1.0, g, device, True) for _ in range(w.steps)]
     out["x_prefix"] = device_normal((w.prefix_len, D), 1.0, g, device, True)
+    return out
+
+
+def device_loop_inputs(w: Workload, steps: int, device="cuda"):
+    """Device modulation of a ``steps``-step loop (the loop_inputs layout, drawn
+    with the device generator): mods [S, n_mod, 6, D], mod_finals [S, 2, D],
+    mod_of_seg, sigmas (host floats)."""
+    torch = _torch()
+    g = device_generator(w, 2000, device)
+    D = w.D
+    edit = len(w.images) > 1
+    out = {}
+    for name, rows, n_sets in (("mods", 6, steps + (1 if edit else 0)), ("mod_finals", 2, steps)):
+        w_mod = device_normal((rows * D, D), 0.02, g, device)
+        b_mod = device_normal((rows * D,), 0.02, g, device)
+        sets = []
+        for _ in range(n_sets):
+            temb = device_normal((D,), 1.0, g, device)
+            sets.append((w_mod @ (temb / (1.0 + torch.exp(-temb))) + b_mod).reshape(rows, D))
+        out[name] = torch.stack(sets).contiguous()
+        del w_mod
+    if edit:
+        out["mods"] = torch.stack([out["mods"][[0, 1 + i]] for i in range(steps)]).contiguous()
+        out["mod_of_seg"] = [0] * (len(w.seg_len) - 1) + [1]
+    else:
+        out["mods"] = out["mods"][:, None].contiguous()
+        out["mod_of_seg"] = [0] * len(w.seg_len)
+    out["sigmas"] = [float(v) for v in loop_sigmas(steps)]
     return out

@@ -243,6 +243,74 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
                       void* const* v_caches, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/* ------------------------------------------------------------------ one velocity evaluation */
+
+/*
+ * DiT head and tail ([Core AI port, graph contracts]: the DiT maps the packed
+ * latent [N, 64] and the text features [L, 4096] to a velocity [N, 64]).  The
+ * pages give only these shapes; reading used here: txt_in = Linear(C_txt -> D),
+ * img_in = Linear(C_lat -> D), tail = LayerNorm (no affine) of the target rows
+ * modulated by (shift, scale) = mod_final, then proj_out = Linear(D -> C_lat).
+ * Weights are [out, in] row-major in the activation dtype (bf16 in the bf16
+ * and W8A8 modes, f32 in the f32 mode); biases are fp32 (NULL = none).
+ * Caller-owned device memory; not modified.
+ */
+typedef struct {
+    const void* w_txt_in;       /* [D, C_txt] */
+    const float* b_txt_in;      /* [D] */
+    const void* w_img_in;       /* [D, C_lat] */
+    const float* b_img_in;      /* [D] */
+    const void* w_proj_out;     /* [C_lat, D] */
+    const float* b_proj_out;    /* [C_lat] */
+    int32_t C_txt;              /* multiple of 64 */
+    int32_t C_lat;              /* multiple of 64 */
+} dit_head_weights;
+
+/*
+ * The sequence is [text (L_txt) | reference image (R) | target image (N)],
+ * T_k = L_txt + R + N = sum(seg_len).  Either all T_k rows are computed
+ * (T_q == T_k: text rows from txt_feats, reference rows from ref_latent) or
+ * only the target rows (T_q == N), the text and reference K/V then being read
+ * from rows [0, T_k - N) of each block's cache, written by an earlier call with
+ * the same prefix inputs (the prefix rows use a modulation set that does not
+ * change between steps, so both give the same result).  Device pointers unless
+ * noted; caller-owned.
+ */
+typedef struct {
+    const void* txt_feats;      /* [L_txt, C_txt] activation dtype; read only when T_q == T_k */
+    const float* ref_latent;    /* [R, C_lat] fp32; read only when T_q == T_k and R > 0 */
+    const float* latent;        /* [N, C_lat] fp32 target latent (not modified) */
+    int64_t L_txt, R, N;
+    const float* mod;           /* [n_mod, 6, D] modulation sets, as in dit_block_io */
+    int32_t n_mod;
+    const int32_t* mod_of_seg;  /* host [n_seg] */
+    const float* mod_final;     /* [2, D] shift, scale of the tail's adaLN */
+    const float* cos_t;         /* [T_q, 64] RoPE tables of the computed rows */
+    const float* sin_t;
+    const int32_t* seg_len;     /* host [n_seg] */
+    int32_t n_seg;
+    int64_t T_q;                /* T_k or N */
+    void* const* k_caches;      /* host array of n_blocks device caches [T_k, H, 128] */
+    void* const* v_caches;
+    void* vel;                  /* [N, C_lat] activation dtype: the velocity */
+} dit_velocity_io;
+
+/* Workspace of dit_velocity_forward (bytes). */
+size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t N, int32_t C_lat);
+
+/*
+ * One evaluation of the DiT: head -> n_blocks blocks (dit_stack_forward) ->
+ * tail, writing io->vel.  The denoise loop then applies dit_euler_step to the
+ * target latent ([Core AI port, graph contracts]: one Euler update per step).
+ * Enqueues work on `stream` only (no allocation, no synchronization), so one
+ * call can be captured in a HIP graph and replayed with new contents of the
+ * same buffers.  Errors: DIT_E_NULL / DIT_E_SHAPE / DIT_E_UNSUPPORTED /
+ * DIT_E_WORKSPACE / DIT_E_ALIGN before any launch; DIT_E_HIP on launch failure.
+ */
+int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* blocks, int32_t n_blocks,
+                         const dit_head_weights* head, const dit_velocity_io* io, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ tracing */
 
 /* Launch sites of the block, in launch order. */

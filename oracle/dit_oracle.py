@@ -29,7 +29,7 @@ __all__ = [
     "round_bf16", "quantize_rows", "int8_matmul_exact", "w8a8_linear", "linear",
     "adaln_modulate", "qk_rmsnorm", "apply_gain", "block_forward_rows", "rope_positions", "rope_tables", "apply_rope",
     "segment_ids", "allowed_mask", "attention", "gelu_tanh", "block_forward",
-    "quantize_block_weights", "dit_step", "euler_update", "rel_l2", "HEAD_DIM",
+    "quantize_block_weights", "dit_step", "denoise_loop", "euler_update", "rel_l2", "HEAD_DIM",
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
 ]
 
@@ -423,6 +423,66 @@ def dit_step(step_in: Dict[str, np.ndarray], blocks, mod, mod_of_seg, seg_len, c
     vel = _store(linear(hf, step_in["w_proj_out"], step_in["b_proj_out"]), mode)
     return {"latent_next": euler_update(lat, vel, step_in["sigma"], step_in["sigma_next"]),
             "vel": vel, "x_blocks": x}
+
+
+def denoise_loop(loop_in: Dict[str, np.ndarray], blocks, mod_of_seg, seg_len, cos, sin, mode: str,
+                 cache_prefix: bool = False) -> Dict[str, np.ndarray]:
+    """The sampling loop around the DiT ([CoreAI], Graph contracts): each step
+    maps the target latent (with the text features, and for editing the
+    reference latents) to a velocity and makes one Euler update of the target
+    latent, sigma_i -> sigma_{i+1}.
+
+    loop_in: latent [N, C] fp32 (target), txt_feats [L, C_txt], ref_latent
+    [R, C] (R may be 0), the head/tail weights of ``dit_step``, mods
+    [S, n_mod, 6, D], mod_finals [S, 2, D], sigmas [S + 1].  The sequence is
+    [text | references | target]; seg_len covers it and cos/sin [T_k, 64] are
+    the tables of all its rows.  ``blocks`` yields (weights, qweights-or-None).
+
+    cache_prefix: steps after the first compute only the target rows and take
+    the text/reference K/V kept from the first step ([Paiton], prefix reuse).
+    When the prefix segments use a modulation set that is the same at every
+    step this changes nothing (prefix rows never attend to target rows); the
+    default recomputes every row at every step.
+    """
+    lat = np.asarray(loop_in["latent"], np.float64).copy()
+    txt = np.asarray(loop_in["txt_feats"], np.float64)
+    ref = np.asarray(loop_in["ref_latent"], np.float64)
+    L, R, N = txt.shape[0], ref.shape[0], lat.shape[0]
+    T_k = L + R + N
+    sig = [float(v) for v in loop_in["sigmas"]]
+    blocks = list(blocks)
+    caches = None
+    vel = None
+    for i in range(len(sig) - 1):
+        mod = loop_in["mods"][i]
+        full = not (cache_prefix and caches is not None)
+        x_tgt = _store(linear(_store(lat, mode), loop_in["w_img_in"], loop_in["b_img_in"]), mode)
+        if full:
+            parts = []
+            if L:
+                parts.append(_store(linear(txt, loop_in["w_txt_in"], loop_in["b_txt_in"]), mode))
+            if R:
+                parts.append(_store(linear(_store(ref, mode), loop_in["w_img_in"], loop_in["b_img_in"]), mode))
+            x = np.concatenate(parts + [x_tgt], axis=0)
+            c, s = cos, sin
+        else:
+            x = x_tgt
+            c, s = cos[T_k - N:], sin[T_k - N:]
+        kept = []
+        for b, (weights, qweights) in enumerate(blocks):
+            kp, vp = (None, None) if full else caches[b]
+            out = block_forward(x, mod, mod_of_seg, seg_len, c, s, weights, mode,
+                                k_prefix=kp, v_prefix=vp, qweights=qweights)
+            if full:
+                kept.append((out["k"][:T_k - N], out["v"][:T_k - N]))
+            x = out["x_out"]
+        if full:
+            caches = kept
+        mf = np.asarray(loop_in["mod_finals"][i], np.float64)
+        hf = _store(adaln_modulate(x[x.shape[0] - N:], mf[0], mf[1]), mode)
+        vel = _store(linear(hf, loop_in["w_proj_out"], loop_in["b_proj_out"]), mode)
+        lat = euler_update(lat, vel, sig[i], sig[i + 1])
+    return {"latent": lat, "vel": vel}
 
 
 def rel_l2(y, y_ref) -> float:

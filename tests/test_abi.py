@@ -153,3 +153,51 @@ def test_block_validation():
     assert call(cfg, w, io) == 4
     cfg, w, io, keep = _block_args(T_q=0)
     assert call(cfg, w, io, ws=None, wsb=0) == 0       # nothing to compute
+
+
+def _velocity_args(segs=(16, 16, 64), T_q=96, L_txt=16, R=16, N=64, mos=(0, 0, 1), n_mod=2):
+    cfg = dq.BlockConfig(dq.MODE_W8A8, 512, 4, 128, 2048, 1e-6, 1e-6)
+    w = dq.BlockWeightsC(**{n: 256 for n, _ in dq.BlockWeightsC._fields_})
+    head = dq.HeadWeightsC(w_txt_in=256, b_txt_in=256, w_img_in=256, b_img_in=256, w_proj_out=256,
+                           b_proj_out=256, C_txt=512, C_lat=64)
+    sarr = (ctypes.c_int32 * len(segs))(*segs)
+    marr = (ctypes.c_int32 * len(mos))(*mos)
+    kc = (ctypes.c_void_p * 1)(256)
+    vc = (ctypes.c_void_p * 1)(256)
+    io = dq.VelocityIO(txt_feats=256, ref_latent=256, latent=256, L_txt=L_txt, R=R, N=N, mod=256, n_mod=n_mod,
+                       mod_of_seg=ctypes.cast(marr, ctypes.c_void_p), mod_final=256, cos_t=256, sin_t=256,
+                       seg_len=ctypes.cast(sarr, ctypes.c_void_p), n_seg=len(segs), T_q=T_q,
+                       k_caches=ctypes.cast(kc, ctypes.c_void_p), v_caches=ctypes.cast(vc, ctypes.c_void_p), vel=256)
+    return cfg, w, head, io, (sarr, marr, kc, vc)
+
+
+def test_velocity_validation():
+    """dit_velocity_forward rejects bad arguments before any HIP call."""
+    lib = dq.lib()
+    cfg = dq.BlockConfig(dq.MODE_W8A8, 512, 4, 128, 2048, 1e-6, 1e-6)
+    need = lib.dit_velocity_workspace_bytes(ctypes.byref(cfg), 96, 64, 64)
+    assert need > lib.dit_block_workspace_bytes(ctypes.byref(cfg), 96, 96) + 96 * 512 * 2
+
+    def call(cfg, w, head, io, ws=256, wsb=1 << 40):
+        return lib.dit_velocity_forward(ctypes.byref(cfg), ctypes.byref(w), 1, ctypes.byref(head),
+                                        ctypes.byref(io), ws, wsb, S)
+
+    a = _velocity_args(T_q=80)
+    assert call(*a[:4]) == 2                               # T_q neither T_k nor N
+    a = _velocity_args(segs=(16, 16, 60))
+    assert call(*a[:4]) == 2                               # seg_len does not add up to L_txt + R + N
+    a = _velocity_args()
+    a[2].C_lat = 48
+    assert call(*a[:4]) == 5                               # C_lat not a multiple of 64
+    a = _velocity_args()
+    a[3].txt_feats = None
+    assert call(*a[:4]) == 1                               # text rows without features
+    a = _velocity_args(T_q=64)
+    a[3].txt_feats = None
+    a[3].ref_latent = None
+    assert call(*a[:4], ws=256, wsb=16) == 6               # cached step: prefix inputs not needed, workspace small
+    a = _velocity_args()
+    a[3].vel = 264
+    assert call(*a[:4]) == 4                               # misaligned output
+    a = _velocity_args(mos=(0, 0, 2))
+    assert call(*a[:4]) == 2                               # modulation set out of range
