@@ -245,15 +245,16 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
 // compiler rotates them through copies every iteration, and each copy waits
 // for the MFMA pipe).  Two waves per SIMD let one wave's MFMAs run while the
 // other waits on LDS.
-// Software pipeline over K steps of 64 bytes with a 3-slot LDS ring: while the
-// MFMAs of step k run from registers, each wave reads the fragments of step
-// k+1 from LDS, writes step k+2 (staged in registers) into LDS and issues the
-// global loads of step k+3.  One barrier per step; the loop body is
-// branch-free so the scheduler can interleave the four streams.
-// LDS has 32 banks (128 bytes per clock).  Rows are 64 bytes; 16-byte chunk c
-// of row r sits at slot c ^ ((r >> 1) & 3), so the eight rows read or written
-// together by one ds_*_b128 phase hit eight different bank groups.
-constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SLOTS = 3, L_THREADS = 512;
+// Software pipeline over K steps of 64 bytes with a 4-slot LDS ring filled by
+// buffer loads straight into LDS (no register staging, no LDS write
+// instructions): while the MFMAs of step k run from registers, each wave reads
+// the fragments of step k+1 from LDS and issues the loads of step k+3, which
+// have two steps to land.  One barrier per step; the loop body is branch-free
+// so the scheduler can interleave the three streams.
+// LDS has 32 banks.  Rows are 64 bytes; 16-byte chunk c of row r sits at slot
+// c ^ ((r >> 1) & 3), so the eight rows read together by one ds_read_b128
+// phase hit eight different bank groups.
+constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SLOTS = 4, L_THREADS = 512;
 constexpr int L_TILE_BYTES = L_BM * L_BK;               // one operand, one slot
 constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
 
@@ -307,36 +308,38 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     const int lane = tid % kWave, wave = tid / kWave;
     const int wm = wave / 4, wn = wave % 4;
 
-    // Thread t stages chunk (t % 4) of rows t/4 and t/4 + 128 of both operands
-    // (rows beyond M or N are clamped: their products only reach outputs that
-    // are never stored).  32-bit offsets from the uniform bases.
-    const int lrow = tid / 4, lch = tid % 4;
-    uint32_t aoff[2], boff[2];
+    // Operands go from memory straight into the LDS ring (buffer loads with the
+    // lds bit: lane l of a wave's load lands at its M0 base + 16 l).  Wave w's
+    // load i covers 16-byte positions p = (2w + i)*64 + lane of a 256 x 64-byte
+    // tile; the swizzle is applied by choosing the source: position p is slot
+    // p % 4 of row p / 4, i.e. chunk (p % 4) ^ ((row >> 1) & 3) of that row.
+    // Rows beyond M or N are clamped: their products only reach outputs that
+    // are never stored.  32-bit offsets; the K offset of a step is the scalar
+    // soffset.
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(M * lda_b), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(N * Kb), 0x00020000);
+    int aoff[2], boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        aoff[i] = (uint32_t)(min(m0 + lrow + 128 * i, M - 1) * lda_b + lch * 16);
-        boff[i] = (uint32_t)(min(n0 + lrow + 128 * i, N - 1) * Kb + lch * 16);
+        const int p = (wave * 2 + i) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+        aoff[i] = (int)(min(m0 + r, M - 1) * lda_b) + c * 16;
+        boff[i] = (int)(min(n0 + r, N - 1) * Kb) + c * 16;
     }
-    v4i ra[2], rb[2];
+    const int wbase = __builtin_amdgcn_readfirstlane(wave * 2 * 1024);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
     typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
     const int arow = wm * 128 + lane % 16, brow = wn * 64 + lane % 16, chunk = lane / 16;
 
-#define LG_LOAD(step)                                                                   \
-    do {                                                                                \
-        const uint32_t kb0 = (uint32_t)(ks0 + min((step), nk - 1)) * L_BK;               \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                 \
-            ra[i] = *reinterpret_cast<const v4i*>(A + (aoff[i] + kb0));                 \
-            rb[i] = *reinterpret_cast<const v4i*>(W + (boff[i] + kb0));                 \
-        }                                                                               \
-    } while (0)
-#define LG_STORE(step)                                                                  \
-    do {                                                                                \
-        uint8_t* dst = lds + ((step) % L_SLOTS) * L_STAGE_BYTES;                        \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                 \
-            *reinterpret_cast<v4i*>(dst + swz(lrow + 128 * i, lch)) = ra[i];            \
-            *reinterpret_cast<v4i*>(dst + L_TILE_BYTES + swz(lrow + 128 * i, lch)) = rb[i]; \
-        }                                                                               \
+#define LG_DMA(step)                                                                          \
+    do {                                                                                      \
+        const int kb0 = (ks0 + min((step), nk - 1)) * L_BK;                                   \
+        uint8_t* sl = lds + ((step) % L_SLOTS) * L_STAGE_BYTES + wbase;                        \
+        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                       \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(sl + i * 1024), 16, aoff[i], kb0, 0, 0); \
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + L_TILE_BYTES + i * 1024), 16, boff[i], \
+                                                     kb0, 0, 0);                              \
+        }                                                                                     \
     } while (0)
 #define LG_FRAGS(step, fa, fb)                                                          \
     do {                                                                                \
@@ -346,10 +349,12 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
             fa[i] = *reinterpret_cast<const frag_t*>(src + swz(arow + i * 16, chunk));   \
     } while (0)
-#define LG_BARRIER()                                       \
-    do {                                                   \
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); \
-        __builtin_amdgcn_s_barrier();                      \
+// End of a step: this wave's loads of the step after next may stay in flight
+// (4 per thread); everything older has landed in LDS.  Then all waves meet.
+#define LG_BARRIER()                                                             \
+    do {                                                                         \
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)" ::: "memory"); \
+        __builtin_amdgcn_s_barrier();                                            \
     } while (0)
 #define LG_MFMA(fa, fb)                                                                           \
     _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                 \
@@ -359,12 +364,11 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
             else                                                                                  \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
         }
-// interleave: per 8 MFMAs, 3 fragment reads, 1 LDS write, 1 global load
+// interleave: per 8 MFMAs, 3 fragment reads and 1 load into LDS
 #define LG_SCHEDULE()                                                  \
     _Pragma("unroll") for (int q = 0; q < 4; ++q) {                    \
         __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             \
-        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);             \
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             \
     }
 
@@ -374,27 +378,25 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-    // prologue: steps 0 and 1 into LDS, step 2 in registers, fragments of step 0
-    LG_LOAD(0);
-    LG_STORE(0);
-    LG_LOAD(1);
-    LG_STORE(1);
-    LG_LOAD(2);
+    // prologue: steps 0, 1 and 2 in flight, wait for 0 and 1, fragments of step 0
+    LG_DMA(0);
+    LG_DMA(1);
+    LG_DMA(2);
     LG_BARRIER();
     frag_t fa0[8], fb0[4], fa1[8], fb1[4];
     LG_FRAGS(0, fa0, fb0);
 
     // Two steps per iteration so the fragment double buffer needs no copies.
+    // Step kt: loads of step kt+3 (into the slot step kt-1 used), fragments of
+    // step kt+1, MFMAs of step kt; step kt+2 must have landed before the barrier.
     int kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-        LG_STORE(kt + 2);
-        LG_LOAD(kt + 3);
+        LG_DMA(kt + 3);
         LG_FRAGS(kt + 1, fa1, fb1);
         LG_MFMA(fa0, fb0);
         LG_SCHEDULE();
         LG_BARRIER();
-        LG_STORE(kt + 3);
-        LG_LOAD(kt + 4);
+        LG_DMA(kt + 4);
         LG_FRAGS(kt + 2, fa0, fb0);
         LG_MFMA(fa1, fb1);
         LG_SCHEDULE();
@@ -403,9 +405,10 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     if (kt < nk) {
         LG_MFMA(fa0, fb0);
     }
+    // the loads past the last step (clamped) must land before LDS is reused
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-#undef LG_LOAD
-#undef LG_STORE
+#undef LG_DMA
 #undef LG_FRAGS
 #undef LG_BARRIER
 #undef LG_MFMA
@@ -570,8 +573,9 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
 template <bool I8, int EV>
 static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                         const EpiParams& ep, hipStream_t st) {
-    if (use_large(M, N) && lda_b % 16 == 0) {
-        static bool lds_set = false;   // allow 96 KB of dynamic LDS (once per instantiation)
+    // the large kernel addresses each operand with 32-bit buffer offsets
+    if (use_large(M, N) && lda_b % 16 == 0 && M * lda_b < ((int64_t)1 << 31) && N * Kb < ((int64_t)1 << 31)) {
+        static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
             (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
