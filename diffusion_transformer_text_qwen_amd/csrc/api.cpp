@@ -454,18 +454,32 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     RUN(launch_adaln(x, bf, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
         "adaln1");
     }
-    // S2: QKV linear -> qkv (bf16-rounded in bf16 modes)
+    // S2 + S3: QKV linear; Q/K RMSNorm + RoPE and the K/V cache rows.  In the
+    // bf16 modes the norm/RoPE runs in the GEMM's epilogue (the [q|k|v] tile
+    // never goes to memory); fp32 mode stores qkv and runs the separate kernel.
+    const bool fused = bf && aligned16(w->g_q) && aligned16(w->g_k) && aligned16(io->cos_t) && aligned16(io->sin_t);
     {
         EpiParams ep = store_epi(qkv, 3 * D, bf, w->b_qkv);
+        if (fused) {
+            ep.kind = EPI_QKV_ROPE;
+            ep.q_out = qb;
+            ep.k_out = kc;
+            ep.v_out = vc;
+            ep.g_q = w->g_q;
+            ep.g_k = w->g_k;
+            ep.cos_t = io->cos_t;
+            ep.sin_t = io->sin_t;
+            ep.qk_eps = cfg->qk_eps;
+            ep.D = D;
+        }
         ProfScope ps(DIT_SITE_QKV_GEMM, st);
         RUN(gemm(h, a8, sa, w->w_qkv, w->s_qkv, 3 * D, D, ep), "qkv_gemm");
     }
-    // S3: Q/K RMSNorm + RoPE, K/V rows into the cache
-    {
-    ProfScope ps(DIT_SITE_QK_NORM_ROPE, st);
-    RUN(launch_qk_norm_rope(qkv, bf, T, H, w->g_q, w->g_k, io->cos_t, io->sin_t, cfg->qk_eps, qb, kc, D, vc,
-                            D, st),
-        "qk_norm_rope");
+    if (!fused) {
+        ProfScope ps(DIT_SITE_QK_NORM_ROPE, st);
+        RUN(launch_qk_norm_rope(qkv, bf, T, H, w->g_q, w->g_k, io->cos_t, io->sin_t, cfg->qk_eps, qb, kc, D, vc,
+                                D, st),
+            "qk_norm_rope");
     }
     // S4: block-causal attention over the whole cache
     const float scale = 1.0f / std::sqrt(128.0f);

@@ -15,7 +15,91 @@ namespace dit {
 __device__ __forceinline__ float gelu_tanh(float u) { return gelu_tanh_fast(u); }
 
 // Epilogue variants, fixed per kernel instantiation (keeps one path live).
-enum EpiVariant : int { EV_STORE = 0, EV_STORE_ACC = 1, EV_GELU = 2, EV_RESID = 3 };
+enum EpiVariant : int { EV_STORE = 0, EV_STORE_ACC = 1, EV_GELU = 2, EV_RESID = 3, EV_QKV = 4 };
+
+// EPI_QKV_ROPE, first half, on 16 consecutive columns n..n+15 of one row: bias
+// and the bf16 rounding of the stored QKV output; returns their sum of squares
+// (the row's RMSNorm statistic over its head is the sum over 8 such groups).
+__device__ __forceinline__ float qkv_prep16(const EpiParams& ep, int64_t n, float (&v)[16]) {
+    if (ep.bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 b = *reinterpret_cast<const float4*>(ep.bias + n + 4 * q);
+            v[4 * q] += b.x; v[4 * q + 1] += b.y; v[4 * q + 2] += b.z; v[4 * q + 3] += b.w;
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        v[e] = bf16r(v[e]);
+        ss += v[e] * v[e];
+    }
+    return ss;
+}
+
+// Gains and RoPE factors of 16 consecutive columns n..n+15 of row m (loaded
+// ahead of the statistic so their latency overlaps it).
+struct QkvAux {
+    float g[16], cs[8], sn[8];
+};
+__device__ __forceinline__ void qkv_gain16(const EpiParams& ep, int64_t n, QkvAux& a) {
+    const int64_t D = ep.D;
+    const int sec = (int)(n / D);
+    const float* g = (sec == 0 ? ep.g_q : ep.g_k) + (n % 128);
+    if (sec == 2) return;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(g + 4 * q);
+        a.g[4 * q] = t.x; a.g[4 * q + 1] = t.y; a.g[4 * q + 2] = t.z; a.g[4 * q + 3] = t.w;
+    }
+}
+__device__ __forceinline__ void qkv_rope16(const EpiParams& ep, int64_t m, int64_t n, QkvAux& a) {
+    if (n / ep.D == 2) return;
+    const int64_t p = m * 64 + (n % 128) / 2;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const float4 c = *reinterpret_cast<const float4*>(ep.cos_t + p + 4 * q);
+        const float4 s = *reinterpret_cast<const float4*>(ep.sin_t + p + 4 * q);
+        a.cs[4 * q] = c.x; a.cs[4 * q + 1] = c.y; a.cs[4 * q + 2] = c.z; a.cs[4 * q + 3] = c.w;
+        a.sn[4 * q] = s.x; a.sn[4 * q + 1] = s.y; a.sn[4 * q + 2] = s.z; a.sn[4 * q + 3] = s.w;
+    }
+}
+
+// Second half: v passes through; q and k get RMSNorm with the head's sum of
+// squares, cast before the gain multiply, then RoPE on the interleaved pairs,
+// each product rounded to bf16 (the order of the separate norm/RoPE kernel).
+__device__ __forceinline__ void qkv_finish16(const EpiParams& ep, int64_t m, int64_t n, const float (&v)[16],
+                                             float ss_head, const QkvAux& a) {
+    const int64_t D = ep.D;
+    const int sec = (int)(n / D);
+    const int64_t c = n - (int64_t)sec * D;
+    __bf16* dst = reinterpret_cast<__bf16*>(sec == 0 ? ep.q_out : sec == 1 ? ep.k_out : ep.v_out) + m * D + c;
+    v8bf o0, o1;
+    if (sec == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o0[e] = to_bf16(v[e]);
+            o1[e] = to_bf16(v[8 + e]);
+        }
+    } else {
+        const float r = 1.0f / sqrtf(ss_head * (1.0f / 128.0f) + ep.qk_eps);
+        float out[16];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float na = bf16r(bf16r(v[2 * k] * r) * a.g[2 * k]);
+            const float nb = bf16r(bf16r(v[2 * k + 1] * r) * a.g[2 * k + 1]);
+            out[2 * k] = na * a.cs[k] - nb * a.sn[k];
+            out[2 * k + 1] = na * a.sn[k] + nb * a.cs[k];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            o0[e] = to_bf16(out[e]);
+            o1[e] = to_bf16(out[8 + e]);
+        }
+    }
+    reinterpret_cast<v8bf*>(dst)[0] = o0;
+    reinterpret_cast<v8bf*>(dst)[1] = o1;
+}
 
 // Apply the epilogue to one output element; v already holds acc*scales (+bias added here).
 template <int EV>
@@ -272,7 +356,10 @@ struct SplitPlan {
     int32_t S;          // 0: whole tiles with epilogue; >= 2: K splits writing partials
 };
 
-template <bool I8, int EV>
+// WN: waves along N (4: 2 x 4 waves of 128 x 64; 2: 4 x 2 waves of 64 x 128,
+// so that one wave holds whole 128-column heads for the fused QKV epilogue).
+// Either way a wave reads 12 fragments per step and issues 32 MFMAs.
+template <bool I8, int EV, int WN>
 __global__ void __launch_bounds__(L_THREADS, 1)
 gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
                   int64_t M, int64_t N, int64_t Kb, EpiParams ep, SplitPlan sp) {
@@ -306,7 +393,11 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
-    const int wm = wave / 4, wn = wave % 4;
+    static_assert(WN == 4 || WN == 2, "wave grid");
+    static_assert(EV != EV_QKV || WN == 2, "the fused QKV epilogue needs whole heads per wave");
+    constexpr int WTM = L_BM / (8 / WN), WTN = L_BN / WN;   // wave tile
+    constexpr int MF = WTM / 16, NF = WTN / 16;             // 16 x 16 accumulator tiles
+    const int wm = wave / WN, wn = wave % WN;
 
     // Operands go from memory straight into the LDS ring (buffer loads with the
     // lds bit: lane l of a wave's load lands at its M0 base + 16 l).  Wave w's
@@ -329,7 +420,7 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     const int wbase = __builtin_amdgcn_readfirstlane(wave * 2 * 1024);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
     typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
-    const int arow = wm * 128 + lane % 16, brow = wn * 64 + lane % 16, chunk = lane / 16;
+    const int arow = wm * WTM + lane % 16, brow = wn * WTN + lane % 16, chunk = lane / 16;
 
 #define LG_DMA(step)                                                                          \
     do {                                                                                      \
@@ -344,9 +435,9 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 #define LG_FRAGS(step, fa, fb)                                                          \
     do {                                                                                \
         const uint8_t* src = lds + ((step) % L_SLOTS) * L_STAGE_BYTES;                  \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j)                                   \
+        _Pragma("unroll") for (int j = 0; j < NF; ++j)                                  \
             fb[j] = *reinterpret_cast<const frag_t*>(src + L_TILE_BYTES + swz(brow + j * 16, chunk)); \
-        _Pragma("unroll") for (int i = 0; i < 8; ++i)                                   \
+        _Pragma("unroll") for (int i = 0; i < MF; ++i)                                  \
             fa[i] = *reinterpret_cast<const frag_t*>(src + swz(arow + i * 16, chunk));   \
     } while (0)
 // End of a step: this wave's loads of the step after next may stay in flight
@@ -357,8 +448,8 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         __builtin_amdgcn_s_barrier();                                            \
     } while (0)
 #define LG_MFMA(fa, fb)                                                                           \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                 \
-        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                           \
+    _Pragma("unroll") for (int i = 0; i < MF; ++i)                                                \
+        _Pragma("unroll") for (int j = 0; j < NF; ++j) {                                          \
             if constexpr (I8)                                                                     \
                 acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0); \
             else                                                                                  \
@@ -372,18 +463,18 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             \
     }
 
-    acc_t acc[8][4];
+    acc_t acc[MF][NF];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < MF; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+        for (int j = 0; j < NF; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
     // prologue: steps 0, 1 and 2 in flight, wait for 0 and 1, fragments of step 0
     LG_DMA(0);
     LG_DMA(1);
     LG_DMA(2);
     LG_BARRIER();
-    frag_t fa0[8], fb0[4], fa1[8], fb1[4];
+    frag_t fa0[MF], fb0[NF], fa1[MF], fb1[NF];
     LG_FRAGS(0, fa0, fb0);
 
     // Two steps per iteration so the fragment double buffer needs no copies.
@@ -414,16 +505,22 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 #undef LG_MFMA
 #undef LG_SCHEDULE
 
-    // Epilogue: for each 16-row slab i, every wave parks its 16 x 64 slab of
+    // Epilogue: for each 16-row slab i, every wave parks its 16 x WTN slab of
     // accumulators in its own LDS region, then each lane finishes 16
-    // consecutive columns of one row.
-    constexpr int EP_STRIDE = 64 + 4;   // words per slab row (padded)
+    // consecutive columns of one row (LPR lanes per row, RPP rows per pass).
+    constexpr int EP_STRIDE = WTN + 4;   // words per slab row (padded)
+    constexpr int LPR = WTN / 16, RPP = kWave / LPR;
     float* slab = reinterpret_cast<float*>(lds) + wave * 16 * EP_STRIDE;
-    const int er = lane / 4, ec = (lane % 4) * 16;
+    const int er0 = lane / LPR, ec = (lane % LPR) * 16;
+    const int64_t n = n0 + wn * WTN + ec;
+    QkvAux aux;
+    if constexpr (EV == EV_QKV) {
+        if (split < 0) qkv_gain16(ep, n, aux);
+    }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MF; ++i) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NF; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (I8)
@@ -433,49 +530,64 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
                     slab[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
             }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if constexpr (I8) {
-            if (split >= 0) {
-                // partial sums of this K range, row-major 256 x 256 per (tile, split)
-                int32_t* part = ep.split_partial +
-                                ((int64_t)(bid - sp.tau0) * sp.S + split) * (L_BM * L_BN) +
-                                (wm * 128 + i * 16 + er) * L_BN + wn * 64 + ec;
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<v4i*>(part + 4 * q) = *reinterpret_cast<const v4i*>(
-                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                continue;
-            }
-        }
-        const int64_t m = m0 + wm * 128 + i * 16 + er;
-        const int64_t n = n0 + wn * 64 + ec;
-        float v[16];
-        int32_t ai[16];
-        if (m < M && n < N) {
+        for (int pass = 0; pass < 16 / RPP; ++pass) {
+            const int er = pass * RPP + er0;
+            const int64_t m = m0 + wm * WTM + i * 16 + er;
             if constexpr (I8) {
-                const float sa = ep.a_scale[m];
+                if (split >= 0) {
+                    // partial sums of this K range, row-major 256 x 256 per (tile, split)
+                    int32_t* part = ep.split_partial +
+                                    ((int64_t)(bid - sp.tau0) * sp.S + split) * (L_BM * L_BN) +
+                                    (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4i t = *reinterpret_cast<const v4i*>(
-                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                    const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ai[4 * q + e] = t[e];
-                        v[4 * q + e] = (float)t[e] * sa * sw[e];
-                    }
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<v4i*>(part + 4 * q) = *reinterpret_cast<const v4i*>(
+                            reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                    continue;
                 }
-            } else {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const v4f t = *reinterpret_cast<const v4f*>(slab + er * EP_STRIDE + ec + 4 * q);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) v[4 * q + e] = t[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 16; ++e) ai[e] = 0;
             }
-            epilogue16<EV>(ep, m, n, v, ai);
+            float v[16];
+            int32_t ai[16];
+            const bool ok = m < M && n < N;
+            if constexpr (EV == EV_QKV) {
+                if (ok) qkv_rope16(ep, m, n, aux);
+            }
+            if (ok) {
+                if constexpr (I8) {
+                    const float sa = ep.a_scale[m];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4i t = *reinterpret_cast<const v4i*>(
+                            reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                        const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            ai[4 * q + e] = t[e];
+                            v[4 * q + e] = (float)t[e] * sa * sw[e];
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const v4f t = *reinterpret_cast<const v4f*>(slab + er * EP_STRIDE + ec + 4 * q);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v[4 * q + e] = t[e];
+                    }
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) ai[e] = 0;
+                }
+            }
+            if constexpr (EV == EV_QKV) {
+                // a head's 128 columns are this wave's 8 lanes of the row
+                float ss = ok ? qkv_prep16(ep, n, v) : 0.0f;
+                ss += dpp_f<0xB1>(ss);
+                ss += dpp_f<0x4E>(ss);
+                ss += __shfl_xor(ss, 4, kWave);
+                if (ok) qkv_finish16(ep, m, n, v, ss, aux);
+            } else {
+                if (ok) epilogue16<EV>(ep, m, n, v, ai);
+            }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
@@ -498,6 +610,7 @@ static unsigned gemm_grid(int64_t M, int64_t N) {
 }
 
 static int variant(const EpiParams& ep) {
+    if (ep.kind == EPI_QKV_ROPE) return EV_QKV;
     if (ep.kind == EPI_GELU) return EV_GELU;
     if (ep.kind == EPI_RESID) return EV_RESID;
     return ep.acc_out ? EV_STORE_ACC : EV_STORE;
@@ -552,6 +665,30 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     if (m >= M || n >= N) return;
     v4i sum[4] = {};
     const int32_t* part = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + row * L_BN + col;
+    if constexpr (EV == EV_QKV) {
+        // 16 threads per row; a head's 128 columns are 8 neighbouring lanes
+        QkvAux aux;
+        qkv_gain16(ep, n, aux);
+        qkv_rope16(ep, m, n, aux);
+        for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+        const float sa = ep.a_scale[m];
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = (float)sum[q][e] * sa * sw[e];
+        }
+        float ss = qkv_prep16(ep, n, v);
+        ss += __shfl_xor(ss, 1, kWave);
+        ss += __shfl_xor(ss, 2, kWave);
+        ss += __shfl_xor(ss, 4, kWave);
+        qkv_finish16(ep, m, n, v, ss, aux);
+        return;
+    }
     for (int s2 = 0; s2 < S; ++s2)
 #pragma unroll
         for (int q = 0; q < 4; ++q) sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
@@ -573,27 +710,36 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
 template <bool I8, int EV>
 static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                         const EpiParams& ep, hipStream_t st) {
+    constexpr int kWN = EV == EV_QKV ? 2 : 4;
     // the large kernel addresses each operand with 32-bit buffer offsets
     if (use_large(M, N) && lda_b % 16 == 0 && M * lda_b < ((int64_t)1 << 31) && N * Kb < ((int64_t)1 << 31)) {
         static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
-            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV>,
+            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
             lds_set = true;
         }
         const int64_t tiles = large_grid(M, N);
         int64_t full = tiles;
         const int S = I8 ? plan_split(tiles, (int)(Kb / L_BK), ep, &full) : 0;
-        gemm_large_kernel<I8, EV><<<(unsigned)full, L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
+        gemm_large_kernel<I8, EV, kWN><<<(unsigned)full, L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
                                                                            SplitPlan{0, (int32_t)full, 0});
         if (S) {
             const int32_t r = (int32_t)(tiles - full);
-            gemm_large_kernel<I8, EV><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
+            gemm_large_kernel<I8, EV, kWN><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
                 a, lda_b, w, M, N, Kb, ep, SplitPlan{(int32_t)full, r, S});
             split_reduce_kernel<EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
         }
     }
-    else
+    else if constexpr (EV == EV_QKV) {
+        // store the QKV output, then the separate norm/RoPE kernel
+        EpiParams e = ep;
+        e.kind = EPI_STORE;
+        e.y_bf16 = 1;
+        gemm_mfma_kernel<I8, EV_STORE><<<gemm_grid(M, N), NTHREADS, 0, st>>>(a, lda_b, w, M, N, Kb, e);
+        (void)launch_qk_norm_rope(ep.y, true, M, (int)(ep.D / 128), ep.g_q, ep.g_k, ep.cos_t, ep.sin_t, ep.qk_eps,
+                                  ep.q_out, ep.k_out, ep.D, ep.v_out, ep.D, st);
+    } else
         gemm_mfma_kernel<I8, EV><<<gemm_grid(M, N), NTHREADS, 0, st>>>(a, lda_b, w, M, N, Kb, ep);
 }
 
@@ -604,6 +750,7 @@ static void launch_mfma_any(const uint8_t* a, int64_t lda_b, const uint8_t* w, i
         case EV_STORE: launch_mfma<I8, EV_STORE>(a, lda_b, w, M, N, Kb, ep, st); break;
         case EV_STORE_ACC: launch_mfma<I8, EV_STORE_ACC>(a, lda_b, w, M, N, Kb, ep, st); break;
         case EV_GELU: launch_mfma<I8, EV_GELU>(a, lda_b, w, M, N, Kb, ep, st); break;
+        case EV_QKV: launch_mfma<I8, EV_QKV>(a, lda_b, w, M, N, Kb, ep, st); break;
         default: launch_mfma<I8, EV_RESID>(a, lda_b, w, M, N, Kb, ep, st); break;
     }
 }

@@ -6,13 +6,18 @@
 
 namespace dit {
 
-enum EpiKind : int32_t { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2 };
+enum EpiKind : int32_t { EPI_STORE = 0, EPI_GELU = 1, EPI_RESID = 2, EPI_QKV_ROPE = 3 };
 
 // What the GEMM does with each output element v = acc (fp32 or bf16 GEMM) or
 // v = acc * a_scale[m] * w_scale[n] (int8 GEMM), after adding bias[n]:
 //   EPI_STORE: y[m, n] = v (bf16-rounded if y_bf16); acc_out[m, n] = int32 acc.
 //   EPI_GELU:  u = round(v); y[m, n] = round(GELU_tanh(u)).
 //   EPI_RESID: y = round(v); x[m, n] = round(x[m, n] + gate[set(m)][n] * y).
+//   EPI_QKV_ROPE (bf16 storage; N = 3 D, D % 256 == 0): y = round(v) is the
+//     [q | k | v] row of the QKV linear; per 128-wide head of q and k:
+//     RMSNorm, cast, gain, cast, RoPE (cos/sin row m), cast; then q -> q_out,
+//     k -> k_out, v -> v_out (row stride D).  Shapes the large-tile kernel does
+//     not take store y to the y scratch and run the separate norm/RoPE kernel.
 // round() is bf16 rounding when act_bf16, identity in fp32 mode.
 struct EpiParams {
     int32_t kind;
@@ -34,6 +39,16 @@ struct EpiParams {
     // partial tiles of the split launch, read back by the reduce launch.
     int32_t* split_partial;
     int64_t split_bytes;   // capacity of split_partial in bytes
+    // EPI_QKV_ROPE
+    void* q_out;
+    void* k_out;
+    void* v_out;
+    const float* g_q;
+    const float* g_k;
+    const float* cos_t;    // [M, 64]
+    const float* sin_t;
+    float qk_eps;
+    int64_t D;
 };
 
 // Bytes of split scratch the int8 GEMM may use for any shape: at most C tiles x
