@@ -344,53 +344,45 @@ constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
 
 __device__ __forceinline__ int swz(int r, int c) { return r * L_BK + ((c ^ ((r >> 1) & 3)) << 4); }
 
-// Remainder split-K: with T tiles on C compute units, floor(T/C)*C tiles run
-// whole in one launch; each of the r remaining tiles is split into S K ranges
-// run by S workgroups of a second launch, which store int32 partial sums; a
-// third launch adds them (integer addition: exact in any order) and applies
-// the epilogue.  This fills the otherwise mostly idle last round; kernel
-// boundaries order the partial stores before their reads.
-struct SplitPlan {
-    int32_t tau0;       // first tile (in tile order) of this launch
-    int32_t ntiles;     // tiles of this launch
-    int32_t S;          // 0: whole tiles with epilogue; >= 2: K splits writing partials
+// Partial last round: with T tiles on C compute units, the C workgroups of one
+// persistent launch each take floor(T/C) whole tiles; each of the r remaining
+// tiles is split into S K ranges, one per workgroup, which stores its int32
+// partial sums.  A second launch adds the partials (integer addition: exact in
+// any order) and applies the epilogue; the kernel boundary orders the partial
+// stores before their reads.  The K range runs before the whole tiles, so its
+// partial stores overlap them.  For long K loops (more than 64 steps) two
+// launches measured faster: whole tiles, then the K ranges (the same kernel
+// with full = 0).
+struct LargePlan {
+    int32_t full;       // whole tiles of this launch: tile order [0, full)
+    int32_t tail0;      // first split tile (tile order)
+    int32_t r;          // split tiles [tail0, tail0 + r), S K ranges each (S = 0: none)
+    int32_t S;
 };
 
+// Grouped tile order: groups of 8 M-tiles sweep N so that neighbouring tiles
+// share rows of A and W.
+__device__ __forceinline__ void tile_origin(int tau, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int g = tau / per_group;
+    const int first_m = g * GROUP;
+    const int gsize = min(tiles_m - first_m, GROUP);
+    m0 = (int64_t)(first_m + (tau % per_group) % gsize) * L_BM;
+    n0 = (int64_t)((tau % per_group) / gsize) * L_BN;
+}
+
+// One 256 x 256 tile, K steps [ks0, ks0 + nk), by the whole workgroup: with
+// part == NULL the epilogue writes the outputs, else the int32 sums go to the
+// 256 x 256 row-major partial tile at part.
 // WN: waves along N (4: 2 x 4 waves of 128 x 64; 2: 4 x 2 waves of 64 x 128,
 // so that one wave holds whole 128-column heads for the fused QKV epilogue).
 // Either way a wave reads 12 fragments per step and issues 32 MFMAs.
 template <bool I8, int EV, int WN>
-__global__ void __launch_bounds__(L_THREADS, 1)
-gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
-                  int64_t M, int64_t N, int64_t Kb, EpiParams ep, SplitPlan sp) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-
-    const int tiles_m = (int)((M + L_BM - 1) / L_BM);
-    const int tiles_n = (int)((N + L_BN - 1) / L_BN);
-    const int nk_all = (int)(Kb / L_BK);
-    // tile order index and K range of this workgroup
-    int bid = blockIdx.x, split = -1, ks0 = 0, nk = nk_all;
-    if (sp.S == 0) {
-        // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
-        // contiguous range of tiles so that tiles sharing rows of A or W share an L2.
-        const int full = (sp.ntiles / 8) * 8;
-        if (bid < full) bid = (bid % 8) * (full / 8) + bid / 8;
-        bid += sp.tau0;
-    } else {
-        split = bid % sp.S;
-        bid = sp.tau0 + bid / sp.S;
-        ks0 = (int)((int64_t)split * nk_all / sp.S);
-        nk = (int)((int64_t)(split + 1) * nk_all / sp.S) - ks0;
-    }
-    constexpr int GROUP = 8;
-    const int per_group = GROUP * tiles_n;
-    const int g = bid / per_group;
-    const int first_m = g * GROUP;
-    const int gsize = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (bid % per_group) % gsize;
-    const int tn = (bid % per_group) / gsize;
-    const int64_t m0 = (int64_t)tm * L_BM, n0 = (int64_t)tn * L_BN;
-
+__device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_t lda_b,
+                                           const uint8_t* __restrict__ W, int64_t M, int64_t N, int64_t Kb,
+                                           const EpiParams& ep, uint8_t* lds, int64_t m0, int64_t n0, int ks0,
+                                           int nk, int32_t* part) {
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     static_assert(WN == 4 || WN == 2, "wave grid");
@@ -442,10 +434,13 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     } while (0)
 // End of a step: this wave's loads of the step after next may stay in flight
 // (4 per thread); everything older has landed in LDS.  Then all waves meet.
+// The scheduling fences keep each step's MFMAs on their side of the barrier.
 #define LG_BARRIER()                                                             \
     do {                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                       \
         asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)" ::: "memory"); \
         __builtin_amdgcn_s_barrier();                                            \
+        __builtin_amdgcn_sched_barrier(0);                                       \
     } while (0)
 #define LG_MFMA(fa, fb)                                                                           \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                                \
@@ -515,7 +510,7 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     const int64_t n = n0 + wn * WTN + ec;
     QkvAux aux;
     if constexpr (EV == EV_QKV) {
-        if (split < 0) qkv_gain16(ep, n, aux);
+        if (part == nullptr) qkv_gain16(ep, n, aux);
     }
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
@@ -535,14 +530,12 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
             const int er = pass * RPP + er0;
             const int64_t m = m0 + wm * WTM + i * 16 + er;
             if constexpr (I8) {
-                if (split >= 0) {
-                    // partial sums of this K range, row-major 256 x 256 per (tile, split)
-                    int32_t* part = ep.split_partial +
-                                    ((int64_t)(bid - sp.tau0) * sp.S + split) * (L_BM * L_BN) +
-                                    (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
+                if (part != nullptr) {
+                    // partial sums of this K range, row-major 256 x 256
+                    int32_t* pp = part + (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<v4i*>(part + 4 * q) = *reinterpret_cast<const v4i*>(
+                        *reinterpret_cast<v4i*>(pp + 4 * q) = *reinterpret_cast<const v4i*>(
                             reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
                     continue;
                 }
@@ -590,6 +583,48 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    __syncthreads();   // the next tile's loads reuse the LDS of this epilogue
+}
+
+template <bool I8, int EV, int WN>
+__global__ void __launch_bounds__(L_THREADS, 1)
+gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
+                  int64_t M, int64_t N, int64_t Kb, EpiParams ep, LargePlan lp) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tiles_m = (int)((M + L_BM - 1) / L_BM);
+    const int tiles_n = (int)((N + L_BN - 1) / L_BN);
+    const int nk_all = (int)(Kb / L_BK);
+    const int G = gridDim.x, b = blockIdx.x;
+    // Jobs: one K range of a split tile (job cj) and whole tiles, one round of
+    // G per job.  Workgroups are dealt round-robin to the 8 XCDs; with full a
+    // multiple of G, XCD x takes the contiguous tile range [x full/8,
+    // (x+1) full/8) so that tiles sharing rows of A or W share an L2.  One call
+    // site keeps one copy of the tile code.
+    const bool chunk = I8 && lp.S > 0 && b < lp.r * lp.S;
+    const bool xcd = G % 8 == 0 && lp.full % G == 0;
+    const int jobs = (lp.full + G - 1) / G;
+    const int cj = chunk ? 0 : -1;   // job index of the K range
+    for (int j = 0; j < jobs + (chunk ? 1 : 0); ++j) {
+        // keep the epilogue's parameter loads inside the loop (hoisting them
+        // would hold them in registers across the main loop)
+        asm volatile("" ::: "memory");
+        int tau, ks0 = 0, nk = nk_all;
+        int32_t* part = nullptr;
+        const int jw = (chunk && j > cj) ? j - 1 : j;            // whole-tile round
+        if (j == cj) {
+            const int t = b / lp.S, k = b % lp.S;
+            ks0 = (int)((int64_t)k * nk_all / lp.S);
+            nk = (int)((int64_t)(k + 1) * nk_all / lp.S) - ks0;
+            tau = lp.tail0 + t;
+            part = ep.split_partial + ((int64_t)t * lp.S + k) * (L_BM * L_BN);
+        } else {
+            tau = xcd ? (b % 8) * (lp.full / 8) + jw * (G / 8) + b / 8 : jw * G + b;
+            if (tau >= lp.full) continue;
+        }
+        int64_t m0, n0;
+        tile_origin(tau, tiles_m, tiles_n, m0, n0);
+        large_tile<I8, EV, WN>(A, lda_b, W, M, N, Kb, ep, lds, m0, n0, ks0, nk, part);
     }
 }
 
@@ -652,16 +687,10 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     const int tiles_m = (int)((M + L_BM - 1) / L_BM);
     const int tiles_n = (int)((N + L_BN - 1) / L_BN);
     const int local = blockIdx.x / 16, rb = blockIdx.x % 16;
-    const int tau = tau0 + local;
-    constexpr int GROUP = 8;
-    const int per_group = GROUP * tiles_n;
-    const int g = tau / per_group;
-    const int first_m = g * GROUP;
-    const int gsize = min(tiles_m - first_m, GROUP);
-    const int tm = first_m + (tau % per_group) % gsize;
-    const int tn = (tau % per_group) / gsize;
+    int64_t tm0, tn0;
+    tile_origin(tau0 + local, tiles_m, tiles_n, tm0, tn0);
     const int row = rb * 16 + threadIdx.x / 16, col = (threadIdx.x % 16) * 16;
-    const int64_t m = (int64_t)tm * L_BM + row, n = (int64_t)tn * L_BN + col;
+    const int64_t m = tm0 + row, n = tn0 + col;
     if (m >= M || n >= N) return;
     v4i sum[4] = {};
     const int32_t* part = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + row * L_BN + col;
@@ -722,14 +751,20 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
         const int64_t tiles = large_grid(M, N);
         int64_t full = tiles;
         const int S = I8 ? plan_split(tiles, (int)(Kb / L_BK), ep, &full) : 0;
-        gemm_large_kernel<I8, EV, kWN><<<(unsigned)full, L_THREADS, L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
-                                                                           SplitPlan{0, (int32_t)full, 0});
-        if (S) {
-            const int32_t r = (int32_t)(tiles - full);
+        const int32_t r = S ? (int32_t)(tiles - full) : 0;
+        const int C = num_cus();
+        if (S && Kb / L_BK > 64) {
+            // long K loops: whole tiles, then the K ranges of the split tiles
+            gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
+                a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
             gemm_large_kernel<I8, EV, kWN><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
-                a, lda_b, w, M, N, Kb, ep, SplitPlan{(int32_t)full, r, S});
-            split_reduce_kernel<EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
+                a, lda_b, w, M, N, Kb, ep, LargePlan{0, (int32_t)full, r, S});
+        } else {
+            // persistent: one workgroup per compute unit (use_large guarantees tiles >= C)
+            gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, tiles), L_THREADS, L_LDS, st>>>(
+                a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, r, S});
         }
+        if (S) split_reduce_kernel<EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
     }
     else if constexpr (EV == EV_QKV) {
         // store the QKV output, then the separate norm/RoPE kernel
