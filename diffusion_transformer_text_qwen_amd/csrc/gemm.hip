@@ -329,20 +329,24 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
 // compiler rotates them through copies every iteration, and each copy waits
 // for the MFMA pipe).  Two waves per SIMD let one wave's MFMAs run while the
 // other waits on LDS.
-// Software pipeline over K steps of 64 bytes with a 4-slot LDS ring filled by
-// buffer loads straight into LDS (no register staging, no LDS write
-// instructions): while the MFMAs of step k run from registers, each wave reads
-// the fragments of step k+1 from LDS and issues the loads of step k+3, which
-// have two steps to land.  One barrier per step; the loop body is branch-free
-// so the scheduler can interleave the three streams.
-// LDS has 32 banks.  Rows are 64 bytes; 16-byte chunk c of row r sits at slot
-// c ^ ((r >> 1) & 3), so the eight rows read together by one ds_read_b128
+// Software pipeline over K steps of 64 bytes (one MFMA K) grouped in stages of
+// 128 bytes, with a 2-slot LDS ring (one stage per slot) filled by buffer
+// loads straight into LDS (no register staging, no LDS write instructions).
+// A stage row is one whole 128-byte line of A or W: loading only 64 bytes of
+// each row per step measured half the L2-to-CU rate of whole lines (27 vs 52
+// bytes per clock per CU with every CU loading), below the 32 bytes per clock
+// the MFMAs consume.  While the MFMAs of step t run from registers, each wave
+// reads the fragments of step t+1 from LDS; during the second step of stage s
+// it also issues the loads of stage s+2 into the slot stage s used, which
+// then have two steps to land.  One barrier per stage; the loop body is
+// branch-free so the scheduler can interleave the three streams.
+// LDS has 32 banks = 128 bytes, one stage row.  16-byte chunk c of row r sits
+// at slot c ^ (r & 7), so the eight rows read together by one ds_read_b128
 // phase hit eight different bank groups.
-constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SLOTS = 4, L_THREADS = 512;
-constexpr int L_TILE_BYTES = L_BM * L_BK;               // one operand, one slot
+constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SK = 128, L_SLOTS = 2, L_THREADS = 512;
+constexpr int L_TILE_BYTES = L_BM * L_SK;               // one operand, one slot
 constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
 
-__device__ __forceinline__ int swz(int r, int c) { return r * L_BK + ((c ^ ((r >> 1) & 3)) << 4); }
 
 // Partial last round: with T tiles on C compute units, the C workgroups of one
 // persistent launch each take floor(T/C) whole tiles; each of the r remaining
@@ -372,7 +376,7 @@ __device__ __forceinline__ void tile_origin(int tau, int tiles_m, int tiles_n, i
     n0 = (int64_t)((tau % per_group) / gsize) * L_BN;
 }
 
-// One 256 x 256 tile, K steps [ks0, ks0 + nk), by the whole workgroup: with
+// One 256 x 256 tile, K steps [ks0, ks0 + nk) (ks0 and nk even: whole stages), by the whole workgroup: with
 // part == NULL the epilogue writes the outputs, else the int32 sums go to the
 // 256 x 256 row-major partial tile at part.
 // WN: waves along N (4: 2 x 4 waves of 128 x 64; 2: 4 x 2 waves of 64 x 128,
@@ -393,54 +397,63 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 
     // Operands go from memory straight into the LDS ring (buffer loads with the
     // lds bit: lane l of a wave's load lands at its M0 base + 16 l).  Wave w's
-    // load i covers 16-byte positions p = (2w + i)*64 + lane of a 256 x 64-byte
-    // tile; the swizzle is applied by choosing the source: position p is slot
-    // p % 4 of row p / 4, i.e. chunk (p % 4) ^ ((row >> 1) & 3) of that row.
-    // Rows beyond M or N are clamped: their products only reach outputs that
-    // are never stored.  32-bit offsets; the K offset of a step is the scalar
-    // soffset.
+    // load i covers 16-byte positions p = (4w + i)*64 + lane of a 256 x 128-byte
+    // stage, i.e. slot p % 8 of row p / 8; the swizzle is applied by choosing
+    // the source chunk (p % 8) ^ (row & 7).  Each group of 8 lanes thus reads
+    // one whole 128-byte line.  Rows beyond M or N are clamped: their products
+    // only reach outputs that are never stored.  32-bit offsets; the K offset
+    // of a stage is the scalar soffset.
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(M * lda_b), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(N * Kb), 0x00020000);
-    int aoff[2], boff[2];
+    int aoff[4], boff[4];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int p = (wave * 2 + i) * 64 + lane, r = p >> 2, c = (p & 3) ^ ((r >> 1) & 3);
+    for (int i = 0; i < 4; ++i) {
+        const int p = (wave * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
         aoff[i] = (int)(min(m0 + r, M - 1) * lda_b) + c * 16;
         boff[i] = (int)(min(n0 + r, N - 1) * Kb) + c * 16;
     }
-    const int wbase = __builtin_amdgcn_readfirstlane(wave * 2 * 1024);
+    const int wbase = __builtin_amdgcn_readfirstlane(wave * 4 * 1024);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
     typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
-    const int arow = wm * WTM + lane % 16, brow = wn * WTN + lane % 16, chunk = lane / 16;
+    // fragment reads: lane reads chunk (4h + lane / 16) of rows base + lane % 16
+    // (+16 i) in step half h; rows are 16-aligned, so row & 7 = lane & 7
+    const int sw = lane & 7, chunk = lane / 16;
+    const int arow = wm * WTM + lane % 16, brow = wn * WTN + lane % 16;
+    const int aswz0 = arow * L_SK + ((chunk ^ sw) << 4), aswz1 = arow * L_SK + (((4 + chunk) ^ sw) << 4);
+    const int bswz0 = L_TILE_BYTES + brow * L_SK + ((chunk ^ sw) << 4);
+    const int bswz1 = L_TILE_BYTES + brow * L_SK + (((4 + chunk) ^ sw) << 4);
+    const int nst = nk / 2;   // stages (nk is even)
 
-#define LG_DMA(step)                                                                          \
+#define LG_DMA(stage)                                                                         \
     do {                                                                                      \
-        const int kb0 = (ks0 + min((step), nk - 1)) * L_BK;                                   \
-        uint8_t* sl = lds + ((step) % L_SLOTS) * L_STAGE_BYTES + wbase;                        \
-        _Pragma("unroll") for (int i = 0; i < 2; ++i) {                                       \
+        const int kb0 = ks0 * L_BK + (stage) * L_SK;                                          \
+        uint8_t* sl = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES + wbase;                       \
+        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(sl + i * 1024), 16, aoff[i], kb0, 0, 0); \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + L_TILE_BYTES + i * 1024), 16, boff[i], \
                                                      kb0, 0, 0);                              \
         }                                                                                     \
     } while (0)
-#define LG_FRAGS(step, fa, fb)                                                          \
+// fragments of step half H of the stage in slot (stage % 2)
+#define LG_FRAGS(stage, H, fa, fb)                                                      \
     do {                                                                                \
-        const uint8_t* src = lds + ((step) % L_SLOTS) * L_STAGE_BYTES;                  \
+        const uint8_t* src = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES;                 \
         _Pragma("unroll") for (int j = 0; j < NF; ++j)                                  \
-            fb[j] = *reinterpret_cast<const frag_t*>(src + L_TILE_BYTES + swz(brow + j * 16, chunk)); \
+            fb[j] = *reinterpret_cast<const frag_t*>(src + ((H) ? bswz1 : bswz0) + j * 16 * L_SK); \
         _Pragma("unroll") for (int i = 0; i < MF; ++i)                                  \
-            fa[i] = *reinterpret_cast<const frag_t*>(src + swz(arow + i * 16, chunk));   \
+            fa[i] = *reinterpret_cast<const frag_t*>(src + ((H) ? aswz1 : aswz0) + i * 16 * L_SK); \
     } while (0)
-// End of a step: this wave's loads of the step after next may stay in flight
-// (4 per thread); everything older has landed in LDS.  Then all waves meet.
-// The scheduling fences keep each step's MFMAs on their side of the barrier.
-#define LG_BARRIER()                                                             \
-    do {                                                                         \
-        __builtin_amdgcn_sched_barrier(0);                                       \
-        asm volatile("s_waitcnt vmcnt(4)\n\ts_waitcnt lgkmcnt(0)" ::: "memory"); \
-        __builtin_amdgcn_s_barrier();                                            \
-        __builtin_amdgcn_sched_barrier(0);                                       \
+// End of a step: this wave's loads issued since the last stage boundary may
+// stay in flight (VM: 8 per thread, or 0); everything older has landed in LDS.
+// Then all waves meet.  The scheduling fences keep each step's MFMAs on their
+// side of the barrier.
+#define LG_BARRIER(VM)                                                                  \
+    do {                                                                                \
+        __builtin_amdgcn_sched_barrier(0);                                              \
+        asm volatile("s_waitcnt vmcnt(" #VM ")\n\ts_waitcnt lgkmcnt(0)" ::: "memory");  \
+        __builtin_amdgcn_s_barrier();                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                              \
     } while (0)
 #define LG_MFMA(fa, fb)                                                                           \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                                \
@@ -450,13 +463,32 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             else                                                                                  \
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
         }
-// interleave: per 8 MFMAs, 3 fragment reads and 1 load into LDS
-#define LG_SCHEDULE()                                                  \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                    \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             \
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             \
+// interleave: per 8 MFMAs, 3 fragment reads (and 2 loads into LDS when the
+// step issues a stage)
+#define LG_SCHEDULE(LOADS)                                                 \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                 \
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                 \
+        if (LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);      \
     }
+// stage s: step 2s (fragments of step 2s+1), then step 2s+1 (loads of stage
+// s+2 when LOADS, fragments of step 2s+2).  One barrier per stage, after step
+// 2s: stage s+1 has landed for every wave and every read of slot s (stage s)
+// is done, so step 2s+1 may refill slot s and read slot s+1.  Nothing needs a
+// barrier after step 2s+1: the next refill of slot s+1 waits for the barrier
+// after step 2s+2.
+#define LG_PAIR(s, LOADS)                                       \
+    do {                                                        \
+        LG_FRAGS(s, 1, fa1, fb1);                               \
+        LG_MFMA(fa0, fb0);                                      \
+        LG_SCHEDULE(false);                                     \
+        LG_BARRIER(0);                                          \
+        if (LOADS) LG_DMA((s) + 2);                             \
+        LG_FRAGS((s) + 1, 0, fa0, fb0);                         \
+        LG_MFMA(fa1, fb1);                                      \
+        LG_SCHEDULE(LOADS);                                     \
+        __builtin_amdgcn_sched_barrier(0);                      \
+    } while (0)
 
     acc_t acc[MF][NF];
 #pragma unroll
@@ -464,41 +496,31 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
 
-    // prologue: steps 0, 1 and 2 in flight, wait for 0 and 1, fragments of step 0
+    // prologue: stages 0 and 1 in flight, wait for 0, fragments of step 0
     LG_DMA(0);
-    LG_DMA(1);
-    LG_DMA(2);
-    LG_BARRIER();
+    if (nst > 1) {
+        LG_DMA(1);
+        LG_BARRIER(8);
+    } else {
+        LG_BARRIER(0);
+    }
     frag_t fa0[MF], fb0[NF], fa1[MF], fb1[NF];
-    LG_FRAGS(0, fa0, fb0);
+    LG_FRAGS(0, 0, fa0, fb0);
 
-    // Two steps per iteration so the fragment double buffer needs no copies.
-    // Step kt: loads of step kt+3 (into the slot step kt-1 used), fragments of
-    // step kt+1, MFMAs of step kt; step kt+2 must have landed before the barrier.
-    int kt = 0;
-    for (; kt + 1 < nk; kt += 2) {
-        LG_DMA(kt + 3);
-        LG_FRAGS(kt + 1, fa1, fb1);
-        LG_MFMA(fa0, fb0);
-        LG_SCHEDULE();
-        LG_BARRIER();
-        LG_DMA(kt + 4);
-        LG_FRAGS(kt + 2, fa0, fb0);
-        LG_MFMA(fa1, fb1);
-        LG_SCHEDULE();
-        LG_BARRIER();
-    }
-    if (kt < nk) {
-        LG_MFMA(fa0, fb0);
-    }
-    // the loads past the last step (clamped) must land before LDS is reused
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Stages that load stage s+2, then the last two without loads.  The step
+    // after the last reads fragments of a slot nobody uses (harmless).
+    int s = 0;
+    for (; s + 2 < nst; ++s) LG_PAIR(s, true);
+    for (; s < nst; ++s) LG_PAIR(s, false);
+    // every load has landed (the last barrier waited for all); the epilogue
+    // reuses LDS once every wave's fragment reads are done
     __syncthreads();
 #undef LG_DMA
 #undef LG_FRAGS
 #undef LG_BARRIER
 #undef LG_MFMA
 #undef LG_SCHEDULE
+#undef LG_PAIR
 
     // Epilogue: for each 16-row slab i, every wave parks its 16 x WTN slab of
     // accumulators in its own LDS region, then each lane finishes 16
@@ -614,8 +636,9 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         const int jw = (chunk && j > cj) ? j - 1 : j;            // whole-tile round
         if (j == cj) {
             const int t = b / lp.S, k = b % lp.S;
-            ks0 = (int)((int64_t)k * nk_all / lp.S);
-            nk = (int)((int64_t)(k + 1) * nk_all / lp.S) - ks0;
+            // whole 128-byte stages
+            ks0 = 2 * (int)((int64_t)k * (nk_all / 2) / lp.S);
+            nk = 2 * (int)((int64_t)(k + 1) * (nk_all / 2) / lp.S) - ks0;
             tau = lp.tail0 + t;
             part = ep.split_partial + ((int64_t)t * lp.S + k) * (L_BM * L_BN);
         } else {
@@ -741,7 +764,8 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
                         const EpiParams& ep, hipStream_t st) {
     constexpr int kWN = EV == EV_QKV ? 2 : 4;
     // the large kernel addresses each operand with 32-bit buffer offsets
-    if (use_large(M, N) && lda_b % 16 == 0 && M * lda_b < ((int64_t)1 << 31) && N * Kb < ((int64_t)1 << 31)) {
+    if (use_large(M, N) && lda_b % 16 == 0 && Kb % L_SK == 0 && M * lda_b < ((int64_t)1 << 31) &&
+        N * Kb < ((int64_t)1 << 31)) {
         static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
             (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN>,
