@@ -138,8 +138,8 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, int64_t m, int64_t
 // 16-byte aligned rows).  v[] holds acc * scales (int8 GEMM) or the fp32 sums.
 template <int EV>
 __device__ __forceinline__ void epilogue16(const EpiParams& ep, int64_t m, int64_t n0, float (&v)[16],
-                                           const int32_t (&acc)[16]) {
-    if (ep.bias) {
+                                           const int32_t (&acc)[16], bool add_bias = true) {
+    if (add_bias && ep.bias) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float4 b = *reinterpret_cast<const float4*>(ep.bias + n0 + 4 * q);
@@ -514,7 +514,9 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     for (; s < nst; ++s) LG_PAIR(s, false);
     // every load has landed (the last barrier waited for all); the epilogue
     // reuses LDS once every wave's fragment reads are done
-    __syncthreads();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 #undef LG_DMA
 #undef LG_FRAGS
 #undef LG_BARRIER
@@ -533,6 +535,36 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     QkvAux aux;
     if constexpr (EV == EV_QKV) {
         if (part == nullptr) qkv_gain16(ep, n, aux);
+    }
+    // Per-lane column constants (weight scales, bias) and the row scales of
+    // every slab are loaded once, before the first slab, so that no slab
+    // waits on a global load of its own.
+    constexpr int NPASS = 16 / RPP;
+    float colw[16], colb[16], rows_sa[MF][NPASS];
+    if constexpr (EV != EV_QKV) {
+        const bool cb = part == nullptr && n < N && ep.bias != nullptr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const v4f b4 = cb ? *reinterpret_cast<const v4f*>(ep.bias + n + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
+            v4f w4 = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (I8) {
+                if (part == nullptr && n < N) w4 = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                colb[4 * q + e] = b4[e];
+                colw[4 * q + e] = w4[e];
+            }
+        }
+    }
+    if constexpr (I8) {
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass) {
+                const int64_t m = m0 + wm * WTM + i * 16 + pass * RPP + er0;
+                rows_sa[i][pass] = (part == nullptr && m < M) ? ep.a_scale[m] : 0.0f;
+            }
     }
 #pragma unroll
     for (int i = 0; i < MF; ++i) {
@@ -570,16 +602,24 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             }
             if (ok) {
                 if constexpr (I8) {
-                    const float sa = ep.a_scale[m];
+                    const float sa = rows_sa[i][pass];
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const v4i t = *reinterpret_cast<const v4i*>(
                             reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                        const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+                        if constexpr (EV == EV_QKV) {
+                            const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            ai[4 * q + e] = t[e];
-                            v[4 * q + e] = (float)t[e] * sa * sw[e];
+                            for (int e = 0; e < 4; ++e) {
+                                ai[4 * q + e] = t[e];
+                                v[4 * q + e] = (float)t[e] * sa * sw[e];
+                            }
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                ai[4 * q + e] = t[e];
+                                v[4 * q + e] = (float)t[e] * sa * colw[4 * q + e];
+                            }
                         }
                     }
                 } else {
@@ -601,12 +641,19 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
                 ss += __shfl_xor(ss, 4, kWave);
                 if (ok) qkv_finish16(ep, m, n, v, ss, aux);
             } else {
-                if (ok) epilogue16<EV>(ep, m, n, v, ai);
+                if (ok) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[e] += colb[e];
+                    epilogue16<EV>(ep, m, n, v, ai, false);
+                }
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
-    __syncthreads();   // the next tile's loads reuse the LDS of this epilogue
+    // the next tile's loads reuse the LDS of this epilogue; its global stores
+    // may stay in flight
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <bool I8, int EV, int WN>
