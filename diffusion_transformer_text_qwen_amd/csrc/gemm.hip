@@ -578,7 +578,9 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
                 else
                     slab[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
             }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // a wave's LDS accesses execute in order: no wait between its slab writes
+        // and reads (the empty asm keeps the compiler from reordering them)
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int pass = 0; pass < 16 / RPP; ++pass) {
             const int er = pass * RPP + er0;
@@ -648,10 +650,11 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
                 }
             }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        asm volatile("" ::: "memory");
     }
     // the next tile's loads reuse the LDS of this epilogue; its global stores
     // may stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
