@@ -31,6 +31,8 @@ __all__ = [
     "segment_ids", "allowed_mask", "attention", "gelu_tanh", "block_forward",
     "quantize_block_weights", "dit_step", "denoise_loop", "euler_update", "rel_l2", "HEAD_DIM",
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
+    "round_fp8_e4m3", "encode_fp8_e4m3", "decode_fp8_e4m3", "quantize_attn_q", "quantize_attn_k",
+    "quantize_attn_v", "attention_q8", "attention_quantized", "ATTN_KEY_TILE", "FP8_MAX",
 ]
 
 HEAD_DIM = 128
@@ -253,6 +255,143 @@ def attention(q, k, v, seg_len: Sequence[int], scale: Optional[float] = None) ->
     return out
 
 
+# ----------------------------------------------------------------------------- quantized attention
+
+# [Paiton, Runtime precision and quality]: after the first denoising steps the
+# runtime switches to int8 activations and int8/fp8 attention.  The page names
+# the number formats only.  Reading taken here (SageAttention-style):
+#   * Q K^T in int8: Q symmetric per (token, head), K symmetric per (tile of
+#     ATTN_KEY_TILE consecutive keys, head); scales amax/127 in fp32, codes by
+#     an IEEE fp32 division and round-half-even (the rule of quantize_rows);
+#   * P V in fp8 e4m3: V symmetric per (head, channel) over all keys, scale
+#     amax/448; P = exp(S - rowmax) in [0, 1] rounded to e4m3 unscaled;
+#   * O = (sum_j fp8(P_ij) * V_j) / (sum_j P_ij): the normalizer adds the
+#     unrounded probabilities.
+ATTN_KEY_TILE = 64
+FP8_MAX = 448.0
+
+
+def round_fp8_e4m3(x) -> np.ndarray:
+    """Nearest e4m3 value (ties to even), saturating at +-448.
+
+    e4m3 (OCP FP8, "fn" variant): 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+    normal values 2^(e-7) * (1 + m/8) for e = 1..15 (the top code 0x7F is NaN,
+    so 448 = 2^8 * 1.75 is the largest), subnormals 2^-6 * m/8.  On the grid
+    the spacing is 2^(E-3) for |x| in [2^E, 2^(E+1)), E >= -6, and 2^-9 below
+    2^-6.  Saturation above 448 is the reading for out-of-range inputs.
+    """
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                       # a = f * 2^ex, f in [0.5, 1)
+    E = np.maximum(ex.astype(np.int64) - 1, -6)
+    step = np.ldexp(1.0, E - 3)
+    r = np.rint(a / step) * step              # power-of-two division: exact; rint ties to even
+    r = np.minimum(r, FP8_MAX)
+    return np.copysign(r, x)
+
+
+def encode_fp8_e4m3(v) -> np.ndarray:
+    """Byte codes of values already on the e4m3 grid (|v| <= 448)."""
+    v = np.asarray(v, np.float64)
+    a = np.abs(v)
+    sign = (np.signbit(v) & (a > 0)).astype(np.uint8) << 7
+    _, ex = np.frexp(a)
+    E = ex.astype(np.int64) - 1
+    normal = a >= 2.0 ** -6
+    e_field = np.where(normal, E + 7, 0)
+    mant = np.where(normal, a / np.ldexp(1.0, np.where(normal, E, 0)) - 1.0, a / 2.0 ** -6) * 8.0
+    if not np.all(mant == np.rint(mant)) or np.any(a > FP8_MAX):
+        raise ValueError("encode_fp8_e4m3: value not on the e4m3 grid")
+    return (sign | (e_field.astype(np.uint8) << 3) | np.rint(mant).astype(np.uint8)).astype(np.uint8)
+
+
+def decode_fp8_e4m3(c) -> np.ndarray:
+    """Values of e4m3 byte codes (0x7F and 0xFF are NaN)."""
+    c = np.asarray(c, np.uint8).astype(np.int64)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    mag = np.where((c & 0x7F) == 0x7F, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def quantize_attn_q(q) -> Tuple[np.ndarray, np.ndarray]:
+    """q [T, H, d] -> int8 codes [T, H, d] and fp32 scales [T, H] (per token and head)."""
+    return quantize_rows(q)
+
+
+def quantize_attn_k(k, tile: int = ATTN_KEY_TILE) -> Tuple[np.ndarray, np.ndarray]:
+    """k [T_k, H, d] -> int8 codes [T_k, H, d] and fp32 scales [ceil(T_k / tile), H].
+
+    One scale per (tile of consecutive keys, head): amax over the tile's keys and
+    the head's d channels, with the rule of quantize_rows."""
+    k = np.asarray(k, np.float64)
+    T_k, H, d = k.shape
+    nt = (T_k + tile - 1) // tile
+    codes = np.zeros((T_k, H, d), np.int8)
+    scales = np.zeros((nt, H), np.float32)
+    for t in range(nt):
+        blk = k[t * tile:(t + 1) * tile]                     # [n, H, d]
+        flat = np.transpose(blk, (1, 0, 2)).reshape(H, -1)   # per head: all values of the tile
+        qf, sf = quantize_rows(flat)
+        codes[t * tile:(t + 1) * tile] = np.transpose(qf.reshape(H, blk.shape[0], d), (1, 0, 2))
+        scales[t] = sf
+    return codes, scales
+
+
+def quantize_attn_v(v) -> Tuple[np.ndarray, np.ndarray]:
+    """v [T_k, H, d] -> e4m3 values [T_k, H, d] (float64 on the e4m3 grid) and fp32
+    scales [H, d]: s = amax over all keys / 448 per (head, channel), values
+    round_fp8_e4m3(fp32(v / s)) with an IEEE fp32 division; s = 0 gives 0."""
+    v64 = np.asarray(v, np.float64)
+    v32 = v64.astype(np.float32)
+    if not np.array_equal(v32.astype(np.float64), v64):
+        raise ValueError("quantize_attn_v: input not representable in fp32")
+    amax = np.max(np.abs(v32), axis=0)                       # [H, d]
+    s = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    r = (v32 / safe[None]).astype(np.float32)
+    vals = round_fp8_e4m3(r)
+    vals[:, s == 0] = 0.0
+    return vals, s
+
+
+def attention_q8(q8, sq, k8, sk, v8, sv, seg_len: Sequence[int], scale: Optional[float] = None,
+                 tile: int = ATTN_KEY_TILE) -> np.ndarray:
+    """Block-causal attention on quantized operands (the reading above), fp64.
+
+    q8 [T_q, H, d] int8 with sq [T_q, H]; k8 [T_k, H, d] int8 with sk
+    [ceil(T_k/tile), H]; v8 [T_k, H, d] e4m3 values with sv [H, d].  Scores are
+    exact integer dot products times the scales; the softmax is fp64."""
+    q8 = np.asarray(q8, np.float64)
+    k8 = np.asarray(k8, np.float64)
+    v8 = np.asarray(v8, np.float64)
+    T_q, H, d = q8.shape
+    T_k = k8.shape[0]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    allowed = allowed_mask(seg_len, T_q)
+    key_scale = np.asarray(sk, np.float64)[np.arange(T_k) // tile]      # [T_k, H]
+    out = np.empty((T_q, H, d))
+    for h in range(H):
+        acc = q8[:, h, :] @ k8[:, h, :].T                  # integers below 2^53: exact
+        s = acc * np.asarray(sq, np.float64)[:, h, None] * key_scale[None, :, h] * scale
+        s = np.where(allowed, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        p8 = round_fp8_e4m3(p)
+        vd = v8[:, h, :] * np.asarray(sv, np.float64)[h][None, :]
+        out[:, h, :] = (p8 @ vd) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def attention_quantized(q, k, v, seg_len: Sequence[int], scale: Optional[float] = None) -> np.ndarray:
+    """Quantize q, k, v (bf16 or fp32 tensors) as above, then attention_q8."""
+    q8, sq = quantize_attn_q(q)
+    k8, sk = quantize_attn_k(k)
+    v8, sv = quantize_attn_v(v)
+    return attention_q8(q8, sq, k8, sk, v8, sv, seg_len, scale)
+
+
 # ----------------------------------------------------------------------------- MLP
 
 def gelu_tanh(u) -> np.ndarray:
@@ -280,7 +419,8 @@ def _lin(a, name, weights, qweights, mode):
 
 def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
                   k_prefix=None, v_prefix=None, qweights=None,
-                  ln_eps: float = LN_EPS, qk_eps: float = QK_EPS) -> Dict[str, np.ndarray]:
+                  ln_eps: float = LN_EPS, qk_eps: float = QK_EPS,
+                  attn_quant: bool = False) -> Dict[str, np.ndarray]:
     """Forward of one single-stream DiT block on the last T_q rows of the sequence.
 
     x [T_q, D]: the rows computed by this call (the whole sequence, or the target
@@ -298,6 +438,7 @@ def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
       x1 = x + gate1 * (o Wo^T + bo)
       h2 = LN(x1)(1+scale2)+shift2
       x2 = x1 + gate2 * (GELU_tanh(h2 W1^T + b1) W2^T + b2)
+    attn_quant: the attention runs on int8/fp8 operands (``attention_quantized``).
     Returns x_out and the new K/V rows plus intermediates.
     """
     x = np.asarray(x, np.float64)
@@ -320,7 +461,8 @@ def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
         v_all = np.concatenate([np.asarray(v_prefix, np.float64), v], axis=0)
     else:
         k_all, v_all = k, v
-    o = _store(attention(q, k_all, v_all, seg_len), mode).reshape(T_q, D)
+    attend = attention_quantized if attn_quant else attention
+    o = _store(attend(q, k_all, v_all, seg_len), mode).reshape(T_q, D)
     y = _store(_lin(o, "w_o", weights, qweights, mode), mode)
     x1 = _store(x + gate1 * y, mode)
     h2 = _store(adaln_modulate(x1, shift2, scale2, ln_eps), mode)
@@ -426,7 +568,7 @@ def dit_step(step_in: Dict[str, np.ndarray], blocks, mod, mod_of_seg, seg_len, c
 
 
 def denoise_loop(loop_in: Dict[str, np.ndarray], blocks, mod_of_seg, seg_len, cos, sin, mode: str,
-                 cache_prefix: bool = False) -> Dict[str, np.ndarray]:
+                 cache_prefix: bool = False, quant_attn_from: Optional[int] = None) -> Dict[str, np.ndarray]:
     """The sampling loop around the DiT ([CoreAI], Graph contracts): each step
     maps the target latent (with the text features, and for editing the
     reference latents) to a velocity and makes one Euler update of the target
@@ -443,6 +585,10 @@ def denoise_loop(loop_in: Dict[str, np.ndarray], blocks, mod_of_seg, seg_len, co
     When the prefix segments use a modulation set that is the same at every
     step this changes nothing (prefix rows never attend to target rows); the
     default recomputes every row at every step.
+
+    quant_attn_from: steps with index >= this run the attention on int8/fp8
+    operands ([Paiton, Runtime precision and quality]: the first steps keep the
+    original precision); None keeps every step unquantized.
     """
     lat = np.asarray(loop_in["latent"], np.float64).copy()
     txt = np.asarray(loop_in["txt_feats"], np.float64)
@@ -472,7 +618,8 @@ def denoise_loop(loop_in: Dict[str, np.ndarray], blocks, mod_of_seg, seg_len, co
         for b, (weights, qweights) in enumerate(blocks):
             kp, vp = (None, None) if full else caches[b]
             out = block_forward(x, mod, mod_of_seg, seg_len, c, s, weights, mode,
-                                k_prefix=kp, v_prefix=vp, qweights=qweights)
+                                k_prefix=kp, v_prefix=vp, qweights=qweights,
+                                attn_quant=quant_attn_from is not None and i >= quant_attn_from)
             if full:
                 kept.append((out["k"][:T_k - N], out["v"][:T_k - N]))
             x = out["x_out"]
