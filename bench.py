@@ -12,7 +12,13 @@ and replayed (Euler updates between replays).
 
 Also measured (reported under "edit_2048px"): one block of the 2048x2048 edit
 workload, [256 text | 1024 reference | 16384 target], uncached step (17,664
-rows) and the cached step that reuses the prefix K/V (16,384 rows).
+rows) and the cached step that reuses the prefix K/V (16,384 rows), the latter
+also with the int8/fp8 attention.
+
+Also measured (reported under "attn_int8_fp8_1024px"): the same step as the
+timed one with the int8 Q K^T / fp8 P V attention (the pages' later denoising
+steps), and the 40-step loop with the first 7 steps bf16 attention, the rest
+int8/fp8 ("denoise_loop_1024px", key "graph_sched_ms").
 
 Inputs are seeded synthetic tensors (ditsynth); the path runs entirely in the
 HIP library through its C ABI.  value / ms_per_step come from K timed steps
@@ -44,6 +50,7 @@ if ROOT not in sys.path:
 METRIC = "DiT-block tokens/s at 4096/16384 img tokens; int8 GEMM & attn % of MFMA peak"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, published (5.0 POP/s)
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published (2.5 PFLOP/s)
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense fp8 (and int8) MFMA, published (5.0 PFLOP/s)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published (8 TB/s)
 GEMM_SITES = ("qkv_gemm", "out_gemm", "up_gemm", "down_gemm")
 
@@ -166,8 +173,8 @@ def run_stack(args, dq, torch, ditsynth):
     lat = si["latent"].clone()
     sigma, sigma_next = 1.0, 1.0 - 0.98 / 39.0
 
-    def step():
-        loop.velocity(lat, txt_b)
+    def step(quant=False):
+        loop.velocity(lat, txt_b, quant=quant)
         dq.euler_step(lat, loop.vel, sigma, sigma_next)
 
     for _ in range(args.warmup):
@@ -193,10 +200,36 @@ def run_stack(args, dq, torch, ditsynth):
     torch.cuda.synchronize()
     prof = dq.profile_end()
     ms_prof = ev0.elapsed_time(ev1) / args.steps
+    # the same step with the int8/fp8 attention
+    for _ in range(args.warmup):
+        step(True)
+    torch.cuda.synchronize()
+    ev0.record()
+    for _ in range(args.steps):
+        step(True)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_q = ev0.elapsed_time(ev1) / args.steps
+    dq.profile_begin(args.steps * w.n_blocks * 12 + 16)
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    prof_q = dq.profile_end()
+    n_timed = args.steps * w.n_blocks
+    att = prof_q["attention"]
+    att_us = att["ms"] / att["count"] * 1e3
+    att_tf = 4 * D * attn_pairs(w.seg_len, T) / (att_us * 1e-6) / 1e12
+    quant_q = {"ms_per_step": round(ms_q, 3), "block_tokens_per_s": round(w.n_blocks * T / (ms_q * 1e-3), 1),
+               "finite": bool(torch.isfinite(lat).all().item()),
+               "attention_avg_us": round(att_us, 2), "attention_tflops": round(att_tf, 1),
+               "attention_frac_fp8_peak": round(att_tf / PEAK_FP8_TFLOPS, 4),
+               "attn_quant_avg_us": round(prof_q["attn_quant"]["ms"] / prof_q["attn_quant"]["count"] * 1e3, 2),
+               "block_ms_sum_of_launches": round(sum(p["ms"] for p in prof_q.values()) / n_timed, 4)}
+    log(f"int8/fp8 attention step: {quant_q}")
     res_loop = None
     if args.loop_steps:
         res_loop = run_loop(args, torch, ditsynth, w, loop, si["latent"], txt_b, None)
-    return w, ms, ms_prof, prof, ok, res_loop
+    return w, ms, ms_prof, prof, ok, res_loop, quant_q
 
 
 def run_loop(args, torch, ditsynth, w, loop, latent0, txt, ref):
@@ -206,12 +239,13 @@ def run_loop(args, torch, ditsynth, w, loop, latent0, txt, ref):
     li = ditsynth.device_loop_inputs(w, steps)
     cache = len(w.images) > 1
     res = {"steps": steps, "prefix_cached": cache}
-    for label, graph in (("eager", False), ("graph", True)):
+    for label, graph, qfrom in (("eager", False, None), ("graph", True, None), ("graph_sched", True, 7)):
         lat = latent0.clone()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         e0.record()
-        loop.run(lat, txt, ref, li["mods"], li["mod_finals"], li["sigmas"], cache_prefix=cache, graph=graph)
+        loop.run(lat, txt, ref, li["mods"], li["mod_finals"], li["sigmas"], cache_prefix=cache, graph=graph,
+                 quant_attn_from=qfrom)
         e1.record()
         torch.cuda.synchronize()
         res[f"{label}_ms"] = round(e0.elapsed_time(e1), 2)
@@ -247,7 +281,8 @@ def run_edit(args, dq, torch, ditsynth, reps):
     dq.rope_tables(L, w.images, 0, T, cos, sin)
     kc = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
     vc = torch.empty_like(kc)
-    ws = torch.empty(dq.workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
+    cfg_q = dq.block_config("w8a8", D, H, F, attn_quant=True)
+    ws = torch.empty(dq.workspace_bytes(cfg_q, T, T), dtype=torch.uint8, device=dev)
     mod = si["mod"]
     x1 = torch.cat([si["x_prefix"], si["x_target"][0]]).to(torch.bfloat16)
     x2 = si["x_target"][1].to(torch.bfloat16)
@@ -256,10 +291,11 @@ def run_edit(args, dq, torch, ditsynth, reps):
     mos1 = [0, 0, 1]
     mos2 = [0, 0, 2]
     res = {}
-    for label, src, dst, mos, r0 in (("uncached", x1, xa, mos1, 0), ("cached", x2, xb, mos2, P)):
+    for label, src, dst, mos, r0, c in (("uncached", x1, xa, mos1, 0, cfg), ("cached", x2, xb, mos2, P, cfg),
+                                        ("cached_attn_int8_fp8", x2, xb, mos2, P, cfg_q)):
         def call():
             dst.copy_(src)
-            dq.block_forward(cfg, bw, dst, mod, mos, cos[r0:], sin[r0:], w.seg_len, kc, vc, ws)
+            dq.block_forward(c, bw, dst, mod, mos, cos[r0:], sin[r0:], w.seg_len, kc, vc, ws)
         call()
         torch.cuda.synchronize()
         dq.profile_begin(reps * 10 + 4)
@@ -277,6 +313,13 @@ def run_edit(args, dq, torch, ditsynth, reps):
         att_tf = att_flops / (att["ms"] / att["count"] * 1e-3) / 1e12
         gops = sum(gemm_ops(T_q, D, F).values())
         gms = sum(prof[s]["ms"] for s in GEMM_SITES) / reps
+        if label.endswith("int8_fp8"):
+            res[label] = {"rows": T_q, "block_ms": round(blk_ms, 3),
+                          "block_tokens_per_s": round(T_q / (blk_ms * 1e-3), 1),
+                          "attention_us": round(att["ms"] / att["count"] * 1e3, 1),
+                          "attention_tflops": round(att_tf, 1),
+                          "attn_quant_us": round(prof["attn_quant"]["ms"] / prof["attn_quant"]["count"] * 1e3, 1)}
+            continue
         res[label] = {
             "rows": T_q, "block_ms": round(blk_ms, 3),
             "block_tokens_per_s": round(T_q / (blk_ms * 1e-3), 1),
@@ -336,7 +379,7 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe, dq, torch)
         return
-    w, ms, ms_prof, prof, ok, loop = run_stack(args, dq, torch, ditsynth)
+    w, ms, ms_prof, prof, ok, loop, quant_q = run_stack(args, dq, torch, ditsynth)
     T, D, F = w.T, w.D, w.F
     n_timed = args.steps * w.n_blocks
     value = w.n_blocks * T / (ms * 1e-3)
@@ -381,6 +424,7 @@ def main():
         "block_ms_sum_of_launches": round(block_ms, 4),
         "finite": ok,
     }
+    line["attn_int8_fp8_1024px"] = quant_q
     if loop is not None:
         line["denoise_loop_1024px"] = loop
     if not args.no_edit:

@@ -9,7 +9,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from typing import Dict, List, Optional, Sequence
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import torch
 
@@ -34,7 +34,7 @@ class DitError(RuntimeError):
 
 class BlockConfig(ctypes.Structure):
     _fields_ = [("mode", _c_i32), ("D", _c_i32), ("H", _c_i32), ("head_dim", _c_i32), ("F", _c_i32),
-                ("ln_eps", _fp), ("qk_eps", _fp)]
+                ("ln_eps", _fp), ("qk_eps", _fp), ("attn_quant", _c_i32)]
 
 
 class BlockWeightsC(ctypes.Structure):
@@ -73,6 +73,10 @@ _SIGS = {
     "f32_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _c_i64, _vp], ctypes.c_int),
     "block_causal_attention": ([_vp, _vp, _vp, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64,
                                 _c_i64, _c_i64, _c_i64, _vp, _c_i32, _fp, _vp], ctypes.c_int),
+    "dit_attn_q8_bytes": ([_c_i64, _c_i64, _c_i32, _vp], ctypes.c_size_t),
+    "dit_attn_quantize": ([_vp, _vp, _vp, _c_i64, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_size_t,
+                           _vp], ctypes.c_int),
+    "block_causal_attention_q8": ([_vp, _c_i64, _c_i64, _c_i32, _vp, _c_i64, _vp, _c_i32, _fp, _vp], ctypes.c_int),
     "dit_rope_tables": ([_c_i32, _vp, _c_i32, _c_i64, _c_i64, _fp, _vp, _vp, _vp], ctypes.c_int),
     "dit_qk_norm_rope": ([_vp, ctypes.c_int, _c_i64, _c_i32, _vp, _vp, _vp, _vp, _fp, _vp, _vp, _c_i64, _vp,
                           _c_i64, _vp], ctypes.c_int),
@@ -88,7 +92,8 @@ _SIGS = {
                            _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "dit_stack_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), _c_i32,
                            ctypes.POINTER(BlockIO), _vp, _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
-    "dit_velocity_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64, _c_i32], ctypes.c_size_t),
+    "dit_velocity_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64, _c_i64, _c_i32],
+                                     ctypes.c_size_t),
     "dit_velocity_forward": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(BlockWeightsC), _c_i32,
                               ctypes.POINTER(HeadWeightsC), ctypes.POINTER(VelocityIO), _vp, ctypes.c_size_t,
                               _vp], ctypes.c_int),
@@ -184,6 +189,32 @@ def block_causal_attention(q, k, v, o, seg_len: Sequence[int], sm_scale: float =
                                         len(seg_len), sm_scale, _stream(stream)), "block_causal_attention")
 
 
+Q8_PARTS = ("q8", "q_scale", "k8", "k_scale", "v8", "v_scale", "v_amax")
+
+
+def attn_q8_layout(T_q: int, T_k: int, H: int) -> Tuple[int, Dict[str, int]]:
+    """(bytes, {part: byte offset}) of the int8/fp8 attention operand buffer."""
+    offs = (ctypes.c_int64 * 7)()
+    n = int(lib().dit_attn_q8_bytes(T_q, T_k, H, ctypes.cast(offs, _vp)))
+    return n, dict(zip(Q8_PARTS, [int(v) for v in offs]))
+
+
+def attn_quantize(q, k, v, buf, stream=None) -> None:
+    """q [T_q, H, 128], k/v [T_k, H, 128] bf16 -> the operand buffer (uint8 device tensor)."""
+    T_q, H, _ = q.shape
+    T_k = k.shape[0]
+    _check(lib().dit_attn_quantize(_p(q), _p(k), _p(v), T_q, T_k, H, q.stride(0), k.stride(0), v.stride(0),
+                                   _p(buf), buf.numel() * buf.element_size(), _stream(stream)), "dit_attn_quantize")
+
+
+def block_causal_attention_q8(buf, T_q: int, T_k: int, H: int, o, seg_len: Sequence[int], sm_scale: float = 0.0,
+                              stream=None) -> None:
+    """o [T_q, H, 128] bf16 from an operand buffer filled by attn_quantize."""
+    segs = _host_i32(seg_len)
+    _check(lib().block_causal_attention_q8(_p(buf), T_q, T_k, H, _p(o), o.stride(0), ctypes.cast(segs, _vp),
+                                           len(seg_len), sm_scale, _stream(stream)), "block_causal_attention_q8")
+
+
 def rope_tables(text_len: int, grids, row0: int, T_rows: int, cos_out, sin_out, theta: float = 10000.0,
                 stream=None) -> None:
     flat = [int(v) for g in grids for v in g]
@@ -218,7 +249,7 @@ def cast(x, y, stream=None) -> None:
     _check(lib().dit_cast(_p(x), _dt(x), _p(y), _dt(y), x.numel(), _stream(stream)), "dit_cast")
 
 
-N_SITES = 10
+N_SITES = 11
 
 
 def profile_begin(capacity: int) -> None:
@@ -235,8 +266,9 @@ def profile_end() -> Dict[str, Dict[str, float]]:
 
 # ---------------------------------------------------------------- the block
 
-def block_config(mode: str, D: int, H: int, F: int, ln_eps: float = 1e-6, qk_eps: float = 1e-6) -> BlockConfig:
-    return BlockConfig(MODES[mode], D, H, 128, F, ln_eps, qk_eps)
+def block_config(mode: str, D: int, H: int, F: int, ln_eps: float = 1e-6, qk_eps: float = 1e-6,
+                 attn_quant: bool = False) -> BlockConfig:
+    return BlockConfig(MODES[mode], D, H, 128, F, ln_eps, qk_eps, int(bool(attn_quant)))
 
 
 class BlockWeights:
@@ -330,8 +362,10 @@ class HeadWeights:
             C_txt=t["w_txt_in"].shape[1] if t.get("w_txt_in") is not None else 0, C_lat=t["w_img_in"].shape[1])
 
 
-def velocity_workspace_bytes(cfg: BlockConfig, T_q: int, N: int, C_lat: int) -> int:
-    return int(lib().dit_velocity_workspace_bytes(ctypes.byref(cfg), T_q, N, C_lat))
+def velocity_workspace_bytes(cfg: BlockConfig, T_q: int, N: int, C_lat: int, T_k: Optional[int] = None) -> int:
+    """T_k = L_txt + R + N (defaults to T_q, the whole sequence)."""
+    T_k = T_q if T_k is None else T_k
+    return int(lib().dit_velocity_workspace_bytes(ctypes.byref(cfg), T_q, T_k, N, C_lat))
 
 
 def velocity_forward(cfg: BlockConfig, ws: Sequence[BlockWeights], head: HeadWeights, latent, vel, mod,

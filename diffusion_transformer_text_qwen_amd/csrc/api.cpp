@@ -326,15 +326,67 @@ int dit_cast(const void* x, int x_dtype, void* y, int y_dtype, int64_t n, void* 
 
 // ------------------------------------------------------------------ block
 
+size_t dit_attn_q8_bytes(int64_t T_q, int64_t T_k, int32_t H, int64_t* offsets) {
+    if (T_q < 0 || T_k < T_q || H < 1) return 0;
+    const AttnQ8Layout L = attn_q8_layout(T_q, T_k, H);
+    if (offsets) {
+        const size_t o[7] = {L.q8, L.sq, L.k8, L.sk, L.v8, L.sv, L.vamax};
+        for (int i = 0; i < 7; ++i) offsets[i] = (int64_t)o[i];
+    }
+    return L.total;
+}
+
+static int check_q8_shape(int64_t T_q, int64_t T_k, int32_t H) {
+    CHECK(H >= 1 && H <= 65535, DIT_E_SHAPE, "H=%d outside [1, 65535]", H);
+    CHECK(T_q >= 0 && T_q <= T_k, DIT_E_SHAPE, "need 0 <= T_q <= T_k");
+    CHECK(T_k < ((int64_t)1 << 31), DIT_E_UNSUPPORTED, "T_k must be below 2^31");
+    CHECK((int64_t)H * ((T_k + 63) / 64) * 8192 < ((int64_t)1 << 31), DIT_E_UNSUPPORTED,
+          "H * ceil(T_k/64) * 8192 must be below 2^31");
+    return DIT_OK;
+}
+
+int dit_attn_quantize(const void* q, const void* k, const void* v, int64_t T_q, int64_t T_k, int32_t H,
+                      int64_t ldq, int64_t ldk, int64_t ldv, void* buf, size_t buf_bytes, void* stream) {
+    int s = check_q8_shape(T_q, T_k, H);
+    if (s) return s;
+    const int64_t row = (int64_t)H * 128;
+    CHECK(ldq >= row && ldk >= row && ldv >= row, DIT_E_SHAPE, "row strides must be >= H*128");
+    CHECK(ldq % 8 == 0 && ldk % 8 == 0 && ldv % 8 == 0, DIT_E_ALIGN, "row strides must be multiples of 8");
+    CHECK(buf != nullptr && buf_bytes >= dit_attn_q8_bytes(T_q, T_k, H, nullptr), DIT_E_WORKSPACE,
+          "buf needs %zu bytes", dit_attn_q8_bytes(T_q, T_k, H, nullptr));
+    CHECK((T_q == 0 || q) && (T_k == 0 || (k && v)), DIT_E_NULL, "q, k and v must be non-NULL");
+    CHECK(aligned16(q) && aligned16(k) && aligned16(v) && aligned16(buf), DIT_E_ALIGN,
+          "q, k, v and buf must be 16-byte aligned");
+    RUN(launch_attn_quantize(q, k, v, T_q, T_k, H, ldq, ldk, ldv, buf, S(stream)), "attn_quantize");
+    return DIT_OK;
+}
+
+int block_causal_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int32_t H, void* o, int64_t ldo,
+                              const int32_t* seg_len, int32_t n_seg, float sm_scale, void* stream) {
+    int s = check_q8_shape(T_q, T_k, H);
+    if (s) return s;
+    CHECK(ldo >= (int64_t)H * 128 && ldo % 8 == 0 && ldo < ((int64_t)1 << 31), DIT_E_SHAPE,
+          "ldo must be >= H*128, a multiple of 8 and below 2^31");
+    s = check_segs(seg_len, n_seg, T_k);
+    if (s) return s;
+    if (T_q == 0) return DIT_OK;
+    CHECK(buf && o, DIT_E_NULL, "buf and o must be non-NULL");
+    CHECK(aligned16(buf) && aligned16(o), DIT_E_ALIGN, "buf and o must be 16-byte aligned");
+    if (sm_scale <= 0.0f) sm_scale = 1.0f / std::sqrt(128.0f);
+    RUN(launch_attention_q8(buf, T_q, T_k, H, o, ldo, make_attn_segs(seg_len, n_seg), sm_scale, S(stream)),
+        "attention_q8");
+    return DIT_OK;
+}
+
 namespace {
 
 struct Plan {
-    size_t h, a8, sa, qkv, q, o, o8, so, g, g8, sg, split, total;
+    size_t h, a8, sa, qkv, q, o, o8, so, g, g8, sg, split, aq, total;
 };
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
-Plan plan(const dit_block_config* cfg, int64_t T) {
+Plan plan(const dit_block_config* cfg, int64_t T, int64_t T_k) {
     const size_t act = cfg->mode == DIT_MODE_F32 ? 4 : 2;
     const size_t D = cfg->D, F = cfg->F;
     const bool q8 = cfg->mode == DIT_MODE_W8A8;
@@ -357,6 +409,7 @@ Plan plan(const dit_block_config* cfg, int64_t T) {
     p.g8 = take(q8 ? T * F : 0);
     p.sg = take(q8 ? T * 4 : 0);
     p.split = take(q8 ? (size_t)kSplitPartialBytes : 0);
+    p.aq = take(cfg->attn_quant ? attn_q8_layout(T, T_k, cfg->H).total : 0);
     p.total = off;
     return p;
 }
@@ -370,6 +423,9 @@ int check_cfg(const dit_block_config* cfg) {
     CHECK(cfg->F >= 256 && cfg->F % 256 == 0 && cfg->F <= 16384, DIT_E_UNSUPPORTED,
           "F must be a multiple of 256 in [256, 16384]");
     CHECK(cfg->ln_eps >= 0.0f && cfg->qk_eps >= 0.0f, DIT_E_SHAPE, "eps must be >= 0");
+    CHECK(cfg->attn_quant == 0 || cfg->attn_quant == 1, DIT_E_SHAPE, "attn_quant must be 0 or 1");
+    CHECK(cfg->attn_quant == 0 || cfg->mode != DIT_MODE_F32, DIT_E_DTYPE,
+          "int8/fp8 attention needs the bf16 or W8A8 mode");
     return DIT_OK;
 }
 
@@ -413,7 +469,7 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     const bool f32 = mode == DIT_MODE_F32, q8 = mode == DIT_MODE_W8A8;
     const bool bf = !f32;
     const size_t act = f32 ? 4 : 2;
-    const Plan p = plan(cfg, T);
+    const Plan p = plan(cfg, T, io->T_k);
     const int64_t row_off = io->T_k - io->T_q;
     const SegMap sm = make_segmap(io->seg_len, io->mod_of_seg, io->n_seg, row_off);
     const AttnSegs segs = make_attn_segs(io->seg_len, io->n_seg);
@@ -483,7 +539,14 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     }
     // S4: block-causal attention over the whole cache
     const float scale = 1.0f / std::sqrt(128.0f);
-    {
+    if (cfg->attn_quant) {
+        {
+            ProfScope ps(DIT_SITE_ATTN_QUANT, st);
+            RUN(launch_attn_quantize(qb, k_cache, v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st), "attn_quantize");
+        }
+        ProfScope ps(DIT_SITE_ATTENTION, st);
+        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st), "attention_q8");
+    } else {
     ProfScope ps(DIT_SITE_ATTENTION, st);
     if (bf)
         RUN(launch_attention_bf16(qb, k_cache, v_cache, ob, T, io->T_k, H, D, D, D, D, segs, scale, st),
@@ -555,9 +618,8 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
 }  // namespace
 
 size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k) {
-    (void)T_k;
-    if (!cfg || T_q < 0) return 0;
-    return plan(cfg, T_q).total;
+    if (!cfg || T_q < 0 || T_k < T_q) return 0;
+    return plan(cfg, T_q, T_k).total;
 }
 
 int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w, const dit_block_io* io,
@@ -569,7 +631,7 @@ int dit_block_forward(const dit_block_config* cfg, const dit_block_weights* w, c
     s = check_io(cfg, io);
     if (s) return s;
     if (io->T_q == 0) return DIT_OK;
-    const size_t need = plan(cfg, io->T_q).total;
+    const size_t need = plan(cfg, io->T_q, io->T_k).total;
     CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
     CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
     return block_impl(cfg, w, io, io->k_cache, io->v_cache, (uint8_t*)workspace, S(stream));
@@ -594,7 +656,7 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
     s = check_io(cfg, &one);
     if (s) return s;
     if (io->T_q == 0 || n_blocks == 0) return DIT_OK;
-    const size_t need = plan(cfg, io->T_q).total;
+    const size_t need = plan(cfg, io->T_q, io->T_k).total;
     CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
     CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
     for (int b = 0; b < n_blocks; ++b) {
@@ -604,11 +666,12 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
     return DIT_OK;
 }
 
-size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t N, int32_t C_lat) {
-    if (!cfg || T_q < 0 || N < 0 || C_lat < 0) return 0;
+size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k, int64_t N,
+                                    int32_t C_lat) {
+    if (!cfg || T_q < 0 || T_k < T_q || N < 0 || C_lat < 0) return 0;
     const size_t es = cfg->mode == DIT_MODE_F32 ? 4 : 2;
     return up256((size_t)T_q * cfg->D * es) + up256((size_t)T_q * C_lat * es) + up256((size_t)N * cfg->D * es) +
-           plan(cfg, T_q).total;
+           plan(cfg, T_q, T_k).total;
 }
 
 int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* blocks, int32_t n_blocks,
@@ -651,7 +714,7 @@ int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* b
         CHECK(io->k_caches[b] && io->v_caches[b], DIT_E_NULL, "cache of block %d is NULL", b);
         CHECK(aligned16(io->k_caches[b]) && aligned16(io->v_caches[b]), DIT_E_ALIGN, "caches must be 16-byte aligned");
     }
-    const size_t need = dit_velocity_workspace_bytes(cfg, io->T_q, io->N, head->C_lat);
+    const size_t need = dit_velocity_workspace_bytes(cfg, io->T_q, T_k, io->N, head->C_lat);
     CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
     CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
     uint8_t* ws = (uint8_t*)workspace;
@@ -764,7 +827,8 @@ int dit_profile_end(double* ms_out, int64_t* count_out, int32_t n_sites) {
 
 const char* dit_site_name(int32_t site) {
     static const char* names[DIT_N_SITES] = {"adaln1", "qkv_gemm", "qk_norm_rope", "attention", "quant_o",
-                                             "out_gemm", "adaln2", "up_gemm", "quant_g", "down_gemm"};
+                                             "out_gemm", "adaln2", "up_gemm", "quant_g", "down_gemm",
+                                             "attn_quant"};
     return (site >= 0 && site < DIT_N_SITES) ? names[site] : "unknown";
 }
 

@@ -31,16 +31,6 @@ constexpr int VT_BYTES = 128 * VT_STRIDE;
 // only raised when a tile's max exceeds it by more than this, so P <= 2^8.
 constexpr float kRescaleLog2 = 8.0f;
 
-// Keys visible to a query at absolute position pos: [0, end of its segment).
-// Static indices only (keeps the argument struct out of private memory).
-__device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
-    int64_t e = sg.end[0];
-#pragma unroll
-    for (int s = 0; s < kMaxSeg - 1; ++s)
-        if (s < sg.n - 1 && pos >= sg.end[s]) e = sg.end[s + 1];
-    return e;
-}
-
 // Transposed V tile.  Keys are stored in the order the S^T accumulator hands
 // them to a lane for the PV product: within each 16-key block, key k sits at
 // position (k % 4) + 4*((k / 8) % 2) + 8*((k / 4) % 2), so the 8 keys one

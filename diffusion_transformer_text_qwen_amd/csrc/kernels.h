@@ -89,11 +89,34 @@ struct AttnSegs {
     int64_t end[kMaxSeg];
     int32_t n;
 };
+// Keys visible to a query at absolute position pos: [0, end of its segment).
+// Static indices only (keeps the argument struct out of private memory).
+__device__ __forceinline__ int64_t kv_end_of(const AttnSegs& sg, int64_t pos) {
+    int64_t e = sg.end[0];
+#pragma unroll
+    for (int s = 0; s < kMaxSeg - 1; ++s)
+        if (s < sg.n - 1 && pos >= sg.end[s]) e = sg.end[s + 1];
+    return e;
+}
 hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, void* o, int64_t T_q,
                                  int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
                                  int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st);
 hipError_t launch_attention_f32(const float* q, const float* k, const float* v, float* o, int64_t T_q,
                                 int64_t T_k, int H, int64_t ldq, int64_t ldk, int64_t ldv,
                                 int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st);
+
+// Int8 / fp8 attention operands: one buffer holding, at the offsets below,
+// q8 [H][T_q][128] int8, q_scale [H][T_q] f32, k8 [H][nt][64 x 128] int8 tile
+// images, k_scale [H][nt] f32, v8 [H][nt][128 x 64] e4m3 tile images,
+// v_scale [H][128] f32 and v_amax [H][128] u32 (scratch); nt = ceil(T_k/64).
+struct AttnQ8Layout {
+    size_t q8, sq, k8, sk, v8, sv, vamax, total;
+    int64_t nt;
+};
+AttnQ8Layout attn_q8_layout(int64_t T_q, int64_t T_k, int H);
+hipError_t launch_attn_quantize(const void* q, const void* k, const void* v, int64_t T_q, int64_t T_k, int H,
+                                int64_t ldq, int64_t ldk, int64_t ldv, void* buf, hipStream_t st);
+hipError_t launch_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int H, void* o, int64_t ldo,
+                               const AttnSegs& segs, float sm_scale, hipStream_t st);
 
 }  // namespace dit

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 1
+#define DIT_ABI_VERSION 2
 
 typedef enum {
     DIT_OK = 0,
@@ -126,6 +126,51 @@ int block_causal_attention(const void* q, const void* k, const void* v, void* o,
                            int32_t n_seg, float sm_scale, void* stream);
 
 /*
+ * Int8 / fp8 attention ("Qwen_Image-2.1-MXFP4-Paiton", Runtime precision and
+ * quality: after the first denoising steps the runtime runs attention in
+ * int8/fp8; the page names only the formats).  Reading:
+ *   q: int8 symmetric per (token, head), scale amax/127;
+ *   k: int8 symmetric per (tile of 64 consecutive keys, head), scale amax/127;
+ *   v: e4m3 per (head, channel) over all T_k keys, scale amax/448;
+ *   codes by an IEEE fp32 division, round half to even (v saturates at 448);
+ *   scores = exact int32 dot products times sm_scale and the q and k scales;
+ *   P = exp of the score minus a running row maximum (at most 2^8 below the
+ *   final one), rounded to e4m3 for the P V product; the softmax normalizer
+ *   sums the unrounded P; o is bf16.
+ *
+ * dit_attn_q8_bytes: size of the operand buffer for (T_q, T_k, H); if
+ * offsets != NULL writes the byte offsets of its 7 parts (256-aligned):
+ *   [0] q8      int8 [H][T_q][128]
+ *   [1] q_scale f32  [H][T_q]
+ *   [2] k8      int8 [H][nt][64][128], nt = ceil(T_k / 64): per (head, tile) an
+ *               8 KB image, key r's 16-byte chunk c (dims 16c..16c+15) at byte
+ *               r*128 + 16*(c ^ (r & 7)); keys past T_k are 0
+ *   [3] k_scale f32  [H][nt]
+ *   [4] v8      e4m3 [H][nt][128][64]: per (head, tile) an 8 KB image, channel
+ *               row ch at byte ch*64; position p = 32*g + b (g = 0, 1;
+ *               b = 0..31) holds key (b/16)*32 + (b%4) + 8*((b%16)/4) + 4*g of
+ *               the tile, and 16-byte chunk c of the row sits at chunk
+ *               c ^ ((ch >> 1) & 3); keys past T_k are 0
+ *   [5] v_scale f32  [H][128]
+ *   [6] scratch u32  [H][128] (channel amax)
+ *
+ * dit_attn_quantize: fills the buffer from bf16 q [T_q, H, 128] and the bf16
+ * K/V cache [T_k, H, 128] (row strides ldq/ldk/ldv in elements, % 8 == 0,
+ * 16-byte aligned); buf_bytes >= dit_attn_q8_bytes.  Enqueued on `stream`
+ * (no allocation, no memset).
+ *
+ * block_causal_attention_q8: o [T_q, H, 128] bf16 (row stride ldo) from the
+ * buffer, block-causal over seg_len as block_causal_attention.  sm_scale <= 0
+ * means 1/sqrt(128).  Supported: 1 <= H <= 65535, 0 <= T_q <= T_k < 2^31,
+ * H * nt * 8192 < 2^31, 1 <= n_seg <= 16.
+ */
+size_t dit_attn_q8_bytes(int64_t T_q, int64_t T_k, int32_t H, int64_t* offsets);
+int dit_attn_quantize(const void* q, const void* k, const void* v, int64_t T_q, int64_t T_k, int32_t H,
+                      int64_t ldq, int64_t ldk, int64_t ldv, void* buf, size_t buf_bytes, void* stream);
+int block_causal_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int32_t H, void* o, int64_t ldo,
+                              const int32_t* seg_len, int32_t n_seg, float sm_scale, void* stream);
+
+/*
  * 3-axis RoPE tables ("RGBA-Image-2.1 - Core AI port", Graph contracts, RoPE).
  * Sequence = [text (text_len tokens) | image 0 | image 1 | ...]; image k is a
  * grids[2k] x grids[2k+1] (h x w) latent grid in raster order (host array).
@@ -187,6 +232,8 @@ typedef struct {
     int32_t F;          /* MLP width */
     float ln_eps;       /* adaLN LayerNorm eps (1e-6) */
     float qk_eps;       /* Q/K RMSNorm eps (1e-6) */
+    int32_t attn_quant; /* 0: bf16/fp32 attention; 1: int8 Q K^T and fp8 P V
+                           (block_causal_attention_q8; bf16 and W8A8 modes) */
 } dit_block_config;
 
 typedef struct {
@@ -223,7 +270,7 @@ size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64
  * One single-stream DiT block on the last T_q rows of a T_k-token sequence:
  *   h  = LN(x)(1+scale1)+shift1;  [q|k|v] = h Wqkv^T + b_qkv
  *   q, k <- RoPE(RMSNorm(q, k) * g);  K/V rows -> cache
- *   o  = block-causal attention(q, K cache, V cache)
+ *   o  = block-causal attention(q, K cache, V cache)   (int8/fp8 if cfg->attn_quant)
  *   x1 = x + gate1 * (o Wo^T + b_o)
  *   x  = x1 + gate2 * (GELU_tanh((LN(x1)(1+scale2)+shift2) W1^T + b1) W2^T + b2)
  * Each row uses the modulation set of its segment.  In W8A8 mode the inputs of
@@ -295,8 +342,9 @@ typedef struct {
     void* vel;                  /* [N, C_lat] activation dtype: the velocity */
 } dit_velocity_io;
 
-/* Workspace of dit_velocity_forward (bytes). */
-size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t N, int32_t C_lat);
+/* Workspace of dit_velocity_forward (bytes); T_k = L_txt + R + N. */
+size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k, int64_t N,
+                                    int32_t C_lat);
 
 /*
  * One evaluation of the DiT: head -> n_blocks blocks (dit_stack_forward) ->
@@ -317,7 +365,7 @@ int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* b
 typedef enum {
     DIT_SITE_ADALN1 = 0, DIT_SITE_QKV_GEMM, DIT_SITE_QK_NORM_ROPE, DIT_SITE_ATTENTION,
     DIT_SITE_QUANT_O, DIT_SITE_OUT_GEMM, DIT_SITE_ADALN2, DIT_SITE_UP_GEMM, DIT_SITE_QUANT_G,
-    DIT_SITE_DOWN_GEMM, DIT_N_SITES
+    DIT_SITE_DOWN_GEMM, DIT_SITE_ATTN_QUANT, DIT_N_SITES
 } dit_site_t;
 
 /*

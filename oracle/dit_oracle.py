@@ -32,7 +32,7 @@ __all__ = [
     "quantize_block_weights", "dit_step", "denoise_loop", "euler_update", "rel_l2", "HEAD_DIM",
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
     "round_fp8_e4m3", "encode_fp8_e4m3", "decode_fp8_e4m3", "quantize_attn_q", "quantize_attn_k",
-    "quantize_attn_v", "attention_q8", "attention_quantized", "ATTN_KEY_TILE", "FP8_MAX",
+    "quantize_attn_v", "attention_q8", "attention_q8_bound", "attention_quantized", "ATTN_KEY_TILE", "FP8_MAX",
 ]
 
 HEAD_DIM = 128
@@ -356,31 +356,59 @@ def quantize_attn_v(v) -> Tuple[np.ndarray, np.ndarray]:
     return vals, s
 
 
-def attention_q8(q8, sq, k8, sk, v8, sv, seg_len: Sequence[int], scale: Optional[float] = None,
-                 tile: int = ATTN_KEY_TILE) -> np.ndarray:
-    """Block-causal attention on quantized operands (the reading above), fp64.
-
-    q8 [T_q, H, d] int8 with sq [T_q, H]; k8 [T_k, H, d] int8 with sk
-    [ceil(T_k/tile), H]; v8 [T_k, H, d] e4m3 values with sv [H, d].  Scores are
-    exact integer dot products times the scales; the softmax is fp64."""
+def _q8_probs(q8, sq, k8, sk, seg_len, scale, tile, h):
+    """P = exp(S - rowmax) [T_q, T_k] of head h on the quantized operands (0 where masked)."""
     q8 = np.asarray(q8, np.float64)
     k8 = np.asarray(k8, np.float64)
-    v8 = np.asarray(v8, np.float64)
-    T_q, H, d = q8.shape
+    T_q, _, d = q8.shape
     T_k = k8.shape[0]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     allowed = allowed_mask(seg_len, T_q)
-    key_scale = np.asarray(sk, np.float64)[np.arange(T_k) // tile]      # [T_k, H]
+    key_scale = np.asarray(sk, np.float64)[np.arange(T_k) // tile, h]
+    acc = q8[:, h, :] @ k8[:, h, :].T                      # integers below 2^53: exact
+    s = acc * np.asarray(sq, np.float64)[:, h, None] * key_scale[None, :] * scale
+    s = np.where(allowed, s, -np.inf)
+    return np.exp(s - s.max(axis=1, keepdims=True))
+
+
+def attention_q8(q8, sq, k8, sk, v8, sv, seg_len: Sequence[int], scale: Optional[float] = None,
+                 tile: int = ATTN_KEY_TILE, round_p: bool = True) -> np.ndarray:
+    """Block-causal attention on quantized operands (the reading above), fp64.
+
+    q8 [T_q, H, d] int8 with sq [T_q, H]; k8 [T_k, H, d] int8 with sk
+    [ceil(T_k/tile), H]; v8 [T_k, H, d] e4m3 values with sv [H, d].  Scores are
+    exact integer dot products times the scales; the softmax is fp64.
+    round_p=False keeps P unrounded (the reference for attention_q8_bound)."""
+    v8 = np.asarray(v8, np.float64)
+    T_q, H, d = np.asarray(q8).shape
     out = np.empty((T_q, H, d))
     for h in range(H):
-        acc = q8[:, h, :] @ k8[:, h, :].T                  # integers below 2^53: exact
-        s = acc * np.asarray(sq, np.float64)[:, h, None] * key_scale[None, :, h] * scale
-        s = np.where(allowed, s, -np.inf)
-        p = np.exp(s - s.max(axis=1, keepdims=True))
-        p8 = round_fp8_e4m3(p)
+        p = _q8_probs(q8, sq, k8, sk, seg_len, scale, tile, h)
+        p8 = round_fp8_e4m3(p) if round_p else p
         vd = v8[:, h, :] * np.asarray(sv, np.float64)[h][None, :]
         out[:, h, :] = (p8 @ vd) / p.sum(axis=1, keepdims=True)
+    return out
+
+
+def attention_q8_bound(q8, sq, k8, sk, v8, sv, seg_len: Sequence[int], scale: Optional[float] = None,
+                       tile: int = ATTN_KEY_TILE) -> np.ndarray:
+    """Element-wise bound on |attention_q8(round_p=True) - attention_q8(round_p=False)|
+    for any rounding reference: if P is rounded to e4m3 after scaling by any
+    2^delta >= 1 (a running maximum below the final one), each rounded value is
+    within 2^-4 of it relatively (half of e4m3's 2^-3 mantissa step) or 2^-10
+    absolutely (half the subnormal step 2^-9), and dividing back by 2^delta
+    only shrinks the absolute part.  Hence
+        |err[i, c]| <= (2^-4 sum_j P_ij |v_jc| + 2^-10 sum_j |v_jc|) / sum_j P_ij
+    with the sums over the keys query i sees."""
+    v8 = np.asarray(v8, np.float64)
+    T_q, H, d = np.asarray(q8).shape
+    out = np.empty((T_q, H, d))
+    for h in range(H):
+        p = _q8_probs(q8, sq, k8, sk, seg_len, scale, tile, h)
+        vabs = np.abs(v8[:, h, :] * np.asarray(sv, np.float64)[h][None, :])
+        seen = (p > 0).astype(np.float64)
+        out[:, h, :] = (2.0 ** -4 * (p @ vabs) + 2.0 ** -10 * (seen @ vabs)) / p.sum(axis=1, keepdims=True)
     return out
 
 

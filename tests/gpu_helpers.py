@@ -46,12 +46,12 @@ def rel_l2(a, b):
 class GpuBlock:
     """One block of a workload on the GPU: weights, caches, workspace, RoPE tables."""
 
-    def __init__(self, w, weights=None, block=0):
+    def __init__(self, w, weights=None, block=0, attn_quant=False):
         self.w = w
         self.mode = w.mode
         arrays = weights if weights is not None else ditsynth.block_weights(w, block)
         self.weights = dq.BlockWeights(arrays, w.mode)
-        self.cfg = dq.block_config(w.mode, w.D, w.H, w.F)
+        self.cfg = dq.block_config(w.mode, w.D, w.H, w.F, attn_quant=attn_quant)
         T = w.T
         self.cos = torch.empty((T, 64), dtype=torch.float32, device=DEV)
         self.sin = torch.empty((T, 64), dtype=torch.float32, device=DEV)

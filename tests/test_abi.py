@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dq.exported_symbols())
-    assert lib.dit_abi_version() == 1
+    assert lib.dit_abi_version() == 2
 
 
 def test_status_strings():
@@ -175,7 +175,7 @@ def test_velocity_validation():
     """dit_velocity_forward rejects bad arguments before any HIP call."""
     lib = dq.lib()
     cfg = dq.BlockConfig(dq.MODE_W8A8, 512, 4, 128, 2048, 1e-6, 1e-6)
-    need = lib.dit_velocity_workspace_bytes(ctypes.byref(cfg), 96, 64, 64)
+    need = lib.dit_velocity_workspace_bytes(ctypes.byref(cfg), 96, 96, 64, 64)
     assert need > lib.dit_block_workspace_bytes(ctypes.byref(cfg), 96, 96) + 96 * 512 * 2
 
     def call(cfg, w, head, io, ws=256, wsb=1 << 40):
@@ -201,3 +201,34 @@ def test_velocity_validation():
     assert call(*a[:4]) == 4                               # misaligned output
     a = _velocity_args(mos=(0, 0, 2))
     assert call(*a[:4]) == 2                               # modulation set out of range
+
+
+def test_attn_q8_validation():
+    """Layout of the int8/fp8 attention buffer and the argument checks (no HIP call)."""
+    lib = dq.lib()
+    n, off = dq.attn_q8_layout(200, 330, 3)
+    nt = (330 + 63) // 64
+    sizes = {"q8": 3 * 200 * 128, "q_scale": 3 * 200 * 4, "k8": 3 * nt * 8192, "k_scale": 3 * nt * 4,
+             "v8": 3 * nt * 8192, "v_scale": 3 * 128 * 4, "v_amax": 3 * 128 * 4}
+    order = list(dq.Q8_PARTS)
+    for i, name in enumerate(order):
+        assert off[name] % 256 == 0
+        end = off[name] + sizes[name]
+        assert end <= (off[order[i + 1]] if i + 1 < len(order) else n)
+    assert lib.dit_attn_q8_bytes(5, 4, 1, None) == 0          # T_q > T_k
+    assert lib.dit_attn_q8_bytes(4, 4, 0, None) == 0          # H < 1
+    q = 256
+    assert lib.dit_attn_quantize(q, q, q, 10, 20, 0, 128, 128, 128, q, 1 << 30, S) == 2      # H
+    assert lib.dit_attn_quantize(q, q, q, 10, 20, 1, 64, 128, 128, q, 1 << 30, S) == 2       # ldq < H*128
+    assert lib.dit_attn_quantize(q, q, q, 10, 20, 1, 132, 128, 128, q, 1 << 30, S) == 4      # ldq % 8
+    assert lib.dit_attn_quantize(q, q, q, 10, 20, 1, 128, 128, 128, q, 16, S) == 6           # buffer small
+    assert lib.dit_attn_quantize(q, q, q, 10, 20, 1, 128, 128, 128, None, 1 << 30, S) == 6   # buffer NULL
+    assert lib.dit_attn_quantize(q, q, 264, 10, 20, 1, 128, 128, 128, q, 1 << 30, S) == 4    # v misaligned
+    segs = (ctypes.c_int32 * 2)(8, 12)
+    sp = ctypes.cast(segs, ctypes.c_void_p)
+    assert lib.block_causal_attention_q8(q, 10, 21, 1, q, 128, sp, 2, 0.0, S) == 2          # seg sum != T_k
+    assert lib.block_causal_attention_q8(q, 10, 20, 1, q, 120, sp, 2, 0.0, S) == 2          # ldo < H*128
+    assert lib.block_causal_attention_q8(None, 10, 20, 1, q, 128, sp, 2, 0.0, S) == 1       # buffer NULL
+    assert lib.block_causal_attention_q8(q, 0, 20, 1, None, 128, sp, 2, 0.0, S) == 0        # T_q == 0: no-op
+    cfg = dq.BlockConfig(dq.MODE_F32, 512, 4, 128, 2048, 1e-6, 1e-6, 1)
+    assert lib.dit_block_workspace_bytes(ctypes.byref(cfg), 96, 96) > 0

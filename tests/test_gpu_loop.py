@@ -49,19 +49,19 @@ class Setup:
         return DenoiseLoop(self.cfg, self.blocks, self.head, self.w.seg_len, self.li["mod_of_seg"], self.w.text,
                            self.cos, self.sin, n_mod=self.li["mods"].shape[1])
 
-    def run(self, cache_prefix, graph=False, per_step=False):
+    def run(self, cache_prefix, graph=False, per_step=False, quant_attn_from=None):
         lat = dev(self.li["latent"])
         steps = []
         on_step = (lambda i: (torch.cuda.synchronize(), steps.append(lat.clone()))) if per_step else None
         self.loop().run(lat, self.txt, self.ref, self.mods, self.finals, self.li["sigmas"],
-                        cache_prefix=cache_prefix, graph=graph, on_step=on_step)
+                        cache_prefix=cache_prefix, graph=graph, on_step=on_step, quant_attn_from=quant_attn_from)
         torch.cuda.synchronize()
         return lat, steps
 
-    def oracle(self):
+    def oracle(self, cache_prefix=False, quant_attn_from=None):
         c, s = oracle.rope_tables(oracle.rope_positions(self.w.text, self.w.images))
         return oracle.denoise_loop(self.li, [(a, None) for a in self.wts], self.li["mod_of_seg"], self.w.seg_len,
-                                   c, s, self.mode)
+                                   c, s, self.mode, cache_prefix=cache_prefix, quant_attn_from=quant_attn_from)
 
 
 @pytest.mark.parametrize("mode", ["w8a8", "bf16"])
@@ -108,3 +108,28 @@ def test_graph_replay_equals_eager_every_step(cache_prefix, images, text):
     for i, (x, y) in enumerate(zip(eager, graphed)):
         assert torch.equal(x, y), f"step {i}"
     assert not torch.equal(eager[0], eager[-1])
+
+
+@pytest.mark.parametrize("mode", ["w8a8", "bf16"])
+def test_loop_with_quantized_attention_schedule(mode):
+    """Step 0 with bf16 attention, steps 1-2 with int8/fp8 attention ([text | ref | target],
+    prefix cached after step 0), against the oracle loop with the same schedule."""
+    say("loop attn schedule", mode)
+    st = Setup(mode, 64, ((8, 8), (16, 16)), steps=3)
+    lat, _ = st.run(cache_prefix=True, quant_attn_from=1)
+    ref = st.oracle(cache_prefix=True, quant_attn_from=1)
+    lat0 = st.li["latent"].astype(np.float64)
+    e = rel_l2(host(lat) - lat0, ref["latent"] - lat0)
+    say(f"  latent change rel_l2 {e:.3e}")
+    assert e <= 2.5 * TOL[mode]
+    # the schedule changes the result (the quantized steps really ran)
+    plain, _ = st.run(cache_prefix=True)
+    assert not torch.equal(plain, lat)
+
+
+def test_graph_replay_equals_eager_with_attention_schedule():
+    st = Setup("w8a8", 64, ((8, 8), (16, 16)), steps=5)
+    _, eager = st.run(cache_prefix=True, per_step=True, quant_attn_from=2)
+    _, graphed = st.run(cache_prefix=True, graph=True, per_step=True, quant_attn_from=2)
+    for i, (x, y) in enumerate(zip(eager, graphed)):
+        assert torch.equal(x, y), f"step {i}"

@@ -176,3 +176,35 @@ def test_attention_q8_sees_scales(flip):
     else:
         sv = sv[:, ::-1].copy()
     assert oracle.rel_l2(oracle.attention_q8(q8, sq, k8, sk, v8, sv, [T]), base) > 1e-2
+
+
+def test_attention_q8_bound_covers_any_rounding_reference():
+    """The bound holds for the exact-max rounding and for P rounded after scaling by
+    2^delta (delta in [0, 8], what a running maximum below the final one gives),
+    and it is not vacuous (the rounding error reaches a sizeable part of it)."""
+    rng = np.random.default_rng(10)
+    T, H, d = 160, 2, 128
+    seg_len = [40, 120]
+    q = oracle.round_bf16(rng.standard_normal((T, H, d)) * 1.5)
+    k = oracle.round_bf16(rng.standard_normal((T, H, d)))
+    v = oracle.round_bf16(rng.standard_normal((T, H, d)))
+    q8, sq = oracle.quantize_attn_q(q)
+    k8, sk = oracle.quantize_attn_k(k)
+    v8, sv = oracle.quantize_attn_v(v)
+    exact = oracle.attention_q8(q8, sq, k8, sk, v8, sv, seg_len, round_p=False)
+    rounded = oracle.attention_q8(q8, sq, k8, sk, v8, sv, seg_len)
+    bound = oracle.attention_q8_bound(q8, sq, k8, sk, v8, sv, seg_len)
+    assert np.all(np.abs(rounded - exact) <= bound * (1 + 1e-9))
+    assert np.max(np.abs(rounded - exact) / bound) > 0.2
+    # P rounded relative to a stale maximum: P' = P 2^delta, rounded, scaled back
+    allowed = oracle.allowed_mask(seg_len, T)
+    for h in range(H):
+        key_scale = sk[np.arange(T) // 64, h].astype(np.float64)
+        s = (q8[:, h].astype(np.float64) @ k8[:, h].astype(np.float64).T) * sq[:, h, None] * key_scale / math.sqrt(d)
+        s = np.where(allowed, s, -np.inf)
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        delta = rng.uniform(0, 8 * math.log(2), (T, 1))
+        p8 = oracle.round_fp8_e4m3(p * np.exp(delta)) / np.exp(delta)
+        vd = v8[:, h] * sv[h][None].astype(np.float64)
+        stale = (p8 @ vd) / p.sum(axis=1, keepdims=True)
+        assert np.all(np.abs(stale - exact[:, h]) <= bound[:, h] * (1 + 1e-9))
