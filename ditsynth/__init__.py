@@ -143,6 +143,25 @@ def block_weights(w: Workload, block: int = 0) -> Dict[str, np.ndarray]:
     return out
 
 
+def gated_block_weights(w: Workload, block: int = 0) -> Dict[str, np.ndarray]:
+    """Weights of block ``block`` of the gated-MLP form: w_qk [2D, D], w_v [D, D],
+    w_o [D, D], w_proj [F, D], w_gate [F, D], w_down [D, F] and biases, N(0, 0.02),
+    gains g_q, g_k 1 + N(0, 0.02); every tensor on the bf16 grid (linears that
+    run W8A8 are quantized from these values at load time by each side)."""
+    rng = _streams(w, _S_BLOCK0 + w.n_blocks)[_S_BLOCK0 + block]
+    D, F = w.D, w.F
+    out = {}
+    for name, shape in (("w_qk", (2 * D, D)), ("b_qk", (2 * D,)), ("w_v", (D, D)), ("b_v", (D,)),
+                        ("g_q", (HEAD_DIM,)), ("g_k", (HEAD_DIM,)), ("w_o", (D, D)), ("b_o", (D,)),
+                        ("w_proj", (F, D)), ("b_proj", (F,)), ("w_gate", (F, D)), ("b_gate", (F,)),
+                        ("w_down", (D, F)), ("b_down", (D,))):
+        a = _normal(rng, shape, 0.02)
+        if name.startswith("g_"):
+            a = (a + np.float32(1.0)).astype(np.float32)
+        out[name] = to_bf16_grid(a)
+    return out
+
+
 def _modulation_sets(w: Workload, n_sets: int, rows: int = 6) -> np.ndarray:
     """[n_sets, rows, D] modulation rows, each set from its own timestep embedding."""
     rng = _streams(w, _S_BLOCK0)[_S_MOD]

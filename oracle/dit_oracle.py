@@ -33,6 +33,7 @@ __all__ = [
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
     "round_fp8_e4m3", "encode_fp8_e4m3", "decode_fp8_e4m3", "quantize_attn_q", "quantize_attn_k",
     "quantize_attn_v", "attention_q8", "attention_q8_bound", "attention_quantized", "ATTN_KEY_TILE", "FP8_MAX",
+    "quantize_rows_asym", "w8a8_linear_asym", "block_forward_gated", "GATED_LINEARS",
 ]
 
 HEAD_DIM = 128
@@ -107,6 +108,47 @@ def int8_matmul_exact(qa: np.ndarray, qw: np.ndarray) -> np.ndarray:
         part = qa[:, k0:k0 + 1024].astype(np.float32) @ qw[:, k0:k0 + 1024].astype(np.float32).T
         acc += np.rint(part).astype(np.int64)
     return acc
+
+
+def quantize_rows_asym(a) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Asymmetric per-row int8 quantization with fp32 scales and int32 zero points.
+
+    [FlagOS, Quantization and validation]: activations are quantized dynamically,
+    asymmetric int8 per token/row, fp32 scales.  Reading (the page gives no
+    formula): the range is widened to contain 0, lo = min(row, 0), hi = max(row, 0);
+    s = fp32(hi - lo) / 255 in fp32; zero point z = -128 - rint(lo / s), which
+    lies in [-128, 127]; q = clamp(rint(a / s) + z, -128, 127); IEEE fp32
+    divisions, ties to even; the value a code stands for is (q - z) * s.  An
+    all-zero row gives s = 0, z = 0, q = 0.  Returns (q int8, s float32, z int32).
+    """
+    a64 = np.asarray(a, dtype=np.float64)
+    a32 = a64.astype(np.float32)
+    if not np.array_equal(a32.astype(np.float64), a64):
+        raise ValueError("quantize_rows_asym: input not representable in fp32")
+    lo = np.minimum(np.min(a32, axis=-1), np.float32(0))
+    hi = np.maximum(np.max(a32, axis=-1), np.float32(0))
+    s = ((hi - lo).astype(np.float32) / np.float32(255.0)).astype(np.float32)
+    safe = np.where(s == 0, np.float32(1.0), s).astype(np.float32)
+    z = (-128 - np.rint((lo / safe).astype(np.float32))).astype(np.int64)
+    z = np.clip(z, -128, 127)
+    r = np.rint((a32 / safe[..., None]).astype(np.float32)).astype(np.int64) + z[..., None]
+    q = np.clip(r, -128, 127)
+    q[s == 0] = 0
+    z[s == 0] = 0
+    return q.astype(np.int8), s, z.astype(np.int32)
+
+
+def w8a8_linear_asym(qa, sa, za, qw, sw, bias) -> np.ndarray:
+    """y = (sum_k (qa[m,k] - za[m]) qw[n,k]) * sa[m] * sw[n] + bias[n], fp64.
+
+    The integer sum is the exact int32 product minus the zero point times the
+    weight codes' row sum (both exact integers)."""
+    acc = int8_matmul_exact(qa, qw) - np.asarray(za, np.int64)[:, None] * \
+        np.asarray(qw, np.int64).sum(axis=1)[None, :]
+    y = acc.astype(np.float64) * np.asarray(sa, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+    if bias is not None:
+        y = y + np.asarray(bias, np.float64)[None, :]
+    return y
 
 
 def w8a8_linear(qa, sa, qw, sw, bias) -> np.ndarray:
@@ -500,6 +542,68 @@ def block_forward(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str,
     x2 = _store(x1 + gate2 * y2, mode)
     return {"x_out": x2, "k": k, "v": v, "q": q, "h": h, "qkv": qkv, "o": o,
             "x1": x1, "h2": h2, "u": u, "g": g}
+
+
+GATED_LINEARS = ("w_qk", "w_v", "w_o", "w_proj", "w_gate", "w_down")
+
+
+def block_forward_gated(x, mod, mod_of_seg, seg_len, cos, sin, weights, int8=(), attn_quant: bool = False,
+                        k_prefix=None, v_prefix=None, ln_eps: float = LN_EPS,
+                        qk_eps: float = QK_EPS) -> Dict[str, np.ndarray]:
+    """The block with a gated MLP and a per-linear choice of W8A8 ([FlagOS,
+    Quantization and validation]: Q/K and the MLP proj/gate linears of the middle
+    blocks run W8A8 with asymmetric per-token activations, the rest bf16).
+
+    weights: w_qk [2D, D] (q rows, then k rows), w_v [D, D], w_o [D, D],
+    w_proj [F, D], w_gate [F, D], w_down [D, F] (fp32 masters on the bf16 grid),
+    their biases b_*, and g_q, g_k.  int8: names of the linears that run W8A8
+    (weights quantized symmetric per output channel, activations asymmetric per
+    token, w8a8_linear_asym); every other linear is bf16.  bf16 storage
+    semantics throughout (mode "bf16").
+
+    Reading for the MLP (the page names a proj and a gate module; the other
+    block structure of block_forward is kept):
+      u = h2 W_proj^T + b_proj;  t = h2 W_gate^T + b_gate  (both stored bf16)
+      g = u * GELU_tanh(t)  (stored bf16);  y2 = g W_down^T + b_down
+    """
+    mode = "bf16"
+    x = np.asarray(x, np.float64)
+    T_q, D = x.shape
+    H = D // HEAD_DIM
+    m = _row_mod(mod, mod_of_seg, seg_len, T_q)
+    shift1, scale1, gate1, shift2, scale2, gate2 = (m[:, i, :] for i in range(6))
+
+    def lin(a, name):
+        b = weights["b" + name[1:]]
+        if name in int8:
+            qa, sa, za = quantize_rows_asym(a)
+            qw, sw = quantize_rows(weights[name])
+            return w8a8_linear_asym(qa, sa, za, qw, sw, b)
+        return linear(a, weights[name], b)
+
+    h = _store(adaln_modulate(x, shift1, scale1, ln_eps), mode)
+    qk = _store(lin(h, "w_qk"), mode)
+    v = _store(lin(h, "w_v"), mode).reshape(T_q, H, HEAD_DIM)
+    q = qk[:, :D].reshape(T_q, H, HEAD_DIM)
+    k = qk[:, D:].reshape(T_q, H, HEAD_DIM)
+    q = _store(apply_rope(qk_rmsnorm(q, weights["g_q"], mode, qk_eps), cos, sin), mode)
+    k = _store(apply_rope(qk_rmsnorm(k, weights["g_k"], mode, qk_eps), cos, sin), mode)
+    if k_prefix is not None and len(k_prefix):
+        k_all = np.concatenate([np.asarray(k_prefix, np.float64), k], axis=0)
+        v_all = np.concatenate([np.asarray(v_prefix, np.float64), v], axis=0)
+    else:
+        k_all, v_all = k, v
+    attend = attention_quantized if attn_quant else attention
+    o = _store(attend(q, k_all, v_all, seg_len), mode).reshape(T_q, D)
+    y = _store(lin(o, "w_o"), mode)
+    x1 = _store(x + gate1 * y, mode)
+    h2 = _store(adaln_modulate(x1, shift2, scale2, ln_eps), mode)
+    u = _store(lin(h2, "w_proj"), mode)
+    t = _store(lin(h2, "w_gate"), mode)
+    g = _store(u * gelu_tanh(t), mode)
+    y2 = _store(lin(g, "w_down"), mode)
+    x2 = _store(x1 + gate2 * y2, mode)
+    return {"x_out": x2, "k": k, "v": v, "q": q, "o": o, "u": u, "g": g, "x1": x1}
 
 
 def block_forward_rows(x, mod, mod_of_seg, seg_len, cos, sin, weights, mode: str, rows,
