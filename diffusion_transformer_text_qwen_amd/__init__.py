@@ -42,6 +42,14 @@ class BlockWeightsC(ctypes.Structure):
                                    "b_qkv", "b_o", "b_1", "b_2", "g_q", "g_k")]
 
 
+class LinearC(ctypes.Structure):
+    _fields_ = [("w", _vp), ("s", _vp), ("wsum", _vp), ("b", _vp)]
+
+
+class GatedBlockWeightsC(ctypes.Structure):
+    _fields_ = [(n, LinearC) for n in ("qk", "v", "o", "proj", "gate", "down")] + [("g_q", _vp), ("g_k", _vp)]
+
+
 class BlockIO(ctypes.Structure):
     _fields_ = [("x", _vp), ("mod", _vp), ("n_mod", _c_i32), ("mod_of_seg", _vp), ("cos_t", _vp),
                 ("sin_t", _vp), ("seg_len", _vp), ("n_seg", _c_i32), ("T_q", _c_i64), ("T_k", _c_i64),
@@ -73,6 +81,13 @@ _SIGS = {
     "f32_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _c_i64, _vp], ctypes.c_int),
     "block_causal_attention": ([_vp, _vp, _vp, _vp, ctypes.c_int, _c_i64, _c_i64, _c_i32, _c_i32, _c_i64,
                                 _c_i64, _c_i64, _c_i64, _vp, _c_i32, _fp, _vp], ctypes.c_int),
+    "dit_quantize_rows_asym": ([_vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "dit_int8_colsum": ([_vp, _c_i64, _c_i64, _vp, _vp], ctypes.c_int),
+    "w8a8_linear_asym": ([_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64,
+                          _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "dit_gated_block_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64], ctypes.c_size_t),
+    "dit_block_forward_gated": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(GatedBlockWeightsC),
+                                 ctypes.POINTER(BlockIO), _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "dit_attn_q8_bytes": ([_c_i64, _c_i64, _c_i32, _vp], ctypes.c_size_t),
     "dit_attn_quantize": ([_vp, _vp, _vp, _c_i64, _c_i64, _c_i32, _c_i64, _c_i64, _c_i64, _vp, ctypes.c_size_t,
                            _vp], ctypes.c_int),
@@ -151,6 +166,28 @@ def quantize_rows(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=
     M, K = x.shape
     _check(lib().dit_quantize_rows(_p(x), _dt(x), M, K, x.stride(0), _p(q), _p(scale), _stream(stream)),
            "dit_quantize_rows")
+
+
+def quantize_rows_asym(x, q, scale, zero, stream=None) -> None:
+    """Asymmetric per-row int8 codes of x [M, K] (bf16/f32): q int8, scale f32 [M], zero int32 [M]."""
+    M, K = x.shape
+    _check(lib().dit_quantize_rows_asym(_p(x), _dt(x), M, K, x.stride(0), _p(q), _p(scale), _p(zero),
+                                        _stream(stream)), "dit_quantize_rows_asym")
+
+
+def int8_colsum(w, out, stream=None) -> None:
+    """out[n] = sum_k w[n, k] (int8 [N, K] -> int32 [N])."""
+    N, K = w.shape
+    _check(lib().dit_int8_colsum(_p(w), N, K, _p(out), _stream(stream)), "dit_int8_colsum")
+
+
+def w8a8_linear_asym(a, a_scale, a_zero, w, w_scale, w_sum, bias, y, workspace=None, stream=None) -> None:
+    M, K = a.shape
+    N = w.shape[0]
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().w8a8_linear_asym(_p(a), _p(a_scale), _p(a_zero), M, K, _p(w), _p(w_scale), _p(w_sum), _p(bias), N,
+                                  _p(y), _dt(y), y.stride(0), _p(workspace), wsb, _stream(stream)),
+           "w8a8_linear_asym")
 
 
 def w8a8_linear_workspace_bytes() -> int:
@@ -392,3 +429,62 @@ def velocity_forward(cfg: BlockConfig, ws: Sequence[BlockWeights], head: HeadWei
                                       _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "dit_velocity_forward")
     del mos, segs, kc, vc, arr
+
+
+# ---------------------------------------------------------------- gated-MLP block (per-linear W8A8)
+
+GATED_LINEARS = ("qk", "v", "o", "proj", "gate", "down")
+
+
+def recipe_int8_linears(block: int, n_blocks: int) -> Tuple[str, ...]:
+    """The page's W8A8 scope ("Qwen-Image-2.1 W8A8 - FlagOS for Mac", Quantization
+    and validation): Q/K and the MLP proj/gate linears in blocks 2..n-3 (2..29 of 32)."""
+    return ("qk", "proj", "gate") if 2 <= block <= n_blocks - 3 else ()
+
+
+class GatedBlockWeights:
+    """Device weights of one gated block: arrays w_qk, w_v, w_o, w_proj, w_gate,
+    w_down ([N, K]) with biases b_* and gains g_q, g_k; the linears named in
+    ``int8`` are quantized per output channel on the GPU (codes, scales and the
+    codes' row sums), the others uploaded as bf16."""
+
+    def __init__(self, arrays: Dict, int8: Sequence[str] = (), device="cuda"):
+        self.t: Dict[str, torch.Tensor] = {}
+        self.int8 = tuple(int8)
+        lin = {}
+        for name in GATED_LINEARS:
+            a = torch.as_tensor(arrays["w_" + name])
+            b = torch.as_tensor(arrays["b_" + name]).to(device=device, dtype=torch.float32).contiguous()
+            self.t["b_" + name] = b
+            if name in self.int8:
+                master = a.to(device=device, dtype=torch.float32).contiguous()
+                q = torch.empty(master.shape, dtype=torch.int8, device=device)
+                sc = torch.empty(master.shape[0], dtype=torch.float32, device=device)
+                quantize_rows(master, q, sc)
+                ws = torch.empty(master.shape[0], dtype=torch.int32, device=device)
+                int8_colsum(q, ws)
+                del master
+                self.t.update({"w_" + name: q, "s_" + name: sc, "wsum_" + name: ws})
+                lin[name] = LinearC(w=_p(q), s=_p(sc), wsum=_p(ws), b=_p(b))
+            else:
+                wt = a.to(device=device, dtype=torch.float32).to(torch.bfloat16).contiguous()
+                self.t["w_" + name] = wt
+                lin[name] = LinearC(w=_p(wt), s=None, wsum=None, b=_p(b))
+        for name in ("g_q", "g_k"):
+            self.t[name] = torch.as_tensor(arrays[name]).to(device=device, dtype=torch.float32).contiguous()
+        self.c = GatedBlockWeightsC(**lin, g_q=_p(self.t["g_q"]), g_k=_p(self.t["g_k"]))
+
+
+def gated_workspace_bytes(cfg: BlockConfig, T_q: int, T_k: int) -> int:
+    return int(lib().dit_gated_block_workspace_bytes(ctypes.byref(cfg), T_q, T_k))
+
+
+def block_forward_gated(cfg: BlockConfig, w: GatedBlockWeights, x, mod, mod_of_seg, cos_t, sin_t, seg_len, k_cache,
+                        v_cache, workspace, stream=None) -> None:
+    """x [T_q, D] bf16 updated in place; k_cache/v_cache [T_k, H, 128] bf16."""
+    T_k = int(sum(seg_len))
+    io, keep = _io(x, mod, mod_of_seg, cos_t, sin_t, seg_len, T_k, k_cache, v_cache)
+    _check(lib().dit_block_forward_gated(ctypes.byref(cfg), ctypes.byref(w.c), ctypes.byref(io), _p(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dit_block_forward_gated")
+    del keep

@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libditblock.so")
-SOURCES = ["api.cpp", "elementwise.hip", "gemm.hip", "attention.hip", "attention_q8.hip"]
+SOURCES = ["api.cpp", "elementwise.hip", "gemm.hip", "attention.hip", "attention_q8.hip", "gated.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -185,6 +185,65 @@ int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, con
     return DIT_OK;
 }
 
+int dit_quantize_rows_asym(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                           float* scale, int32_t* zero, void* stream) {
+    CHECK(x_dtype == DIT_BF16 || x_dtype == DIT_F32, DIT_E_DTYPE, "x_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && ldx >= K, DIT_E_SHAPE, "need M>=0, K>=1, ldx>=K");
+    CHECK(K % 8 == 0 && ldx % 8 == 0, DIT_E_UNSUPPORTED, "K and ldx must be multiples of 8");
+    CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
+    if (M == 0) return DIT_OK;
+    CHECK(x && q && scale && zero, DIT_E_NULL, "x, q, scale and zero must be non-NULL");
+    CHECK(aligned16(x) && aligned16(q), DIT_E_ALIGN, "x and q must be 16-byte aligned");
+    RUN(launch_quantize_rows_asym(x, x_dtype == DIT_BF16, M, K, ldx, q, scale, zero, S(stream)),
+        "quantize_rows_asym");
+    return DIT_OK;
+}
+
+int dit_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, void* stream) {
+    CHECK(N >= 0 && K >= 1, DIT_E_SHAPE, "need N>=0, K>=1");
+    CHECK(K % 16 == 0, DIT_E_UNSUPPORTED, "K must be a multiple of 16");
+    CHECK(N <= ((int64_t)1 << 32), DIT_E_UNSUPPORTED, "N too large");
+    if (N == 0) return DIT_OK;
+    CHECK(w && out, DIT_E_NULL, "w and out must be non-NULL");
+    CHECK(aligned16(w), DIT_E_ALIGN, "w must be 16-byte aligned");
+    RUN(launch_int8_colsum(w, N, K, out, S(stream)), "int8_colsum");
+    return DIT_OK;
+}
+
+int w8a8_linear_asym(const int8_t* a, const float* a_scale, const int32_t* a_zero, int64_t M, int64_t K,
+                     const int8_t* w, const float* w_scale, const int32_t* w_sum, const float* bias, int64_t N,
+                     void* y, int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
+    CHECK(a_zero == nullptr || w_sum != nullptr || M == 0, DIT_E_NULL, "a_zero needs w_sum");
+    CHECK(w_sum == nullptr || aligned16(w_sum), DIT_E_ALIGN, "w_sum must be 16-byte aligned");
+    if (a_zero == nullptr)
+        return w8a8_linear(a, a_scale, M, K, w, w_scale, bias, N, y, y_dtype, ldy, nullptr, workspace,
+                           workspace_bytes, stream);
+    CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && N >= 1 && ldy >= N, DIT_E_SHAPE, "need M>=0, K>=1, N>=1, ldy>=N");
+    CHECK(K % 128 == 0, DIT_E_UNSUPPORTED, "K=%lld must be a multiple of 128", (long long)K);
+    CHECK(N % 16 == 0, DIT_E_UNSUPPORTED, "N=%lld must be a multiple of 16", (long long)N);
+    CHECK(K <= 65536, DIT_E_UNSUPPORTED, "K=%lld beyond the int32-safe bound (255 * 127 * K < 2^31)", (long long)K);
+    CHECK(M * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), DIT_E_UNSUPPORTED,
+          "operands must be below 2 GiB");
+    CHECK(workspace == nullptr || workspace_bytes >= w8a8_linear_workspace_bytes(), DIT_E_WORKSPACE,
+          "workspace needs %zu bytes", w8a8_linear_workspace_bytes());
+    if (M == 0) return DIT_OK;
+    CHECK(a && a_scale && w && w_scale && y, DIT_E_NULL, "a, a_scale, w, w_scale and y must be non-NULL");
+    CHECK(aligned16(a) && aligned16(w), DIT_E_ALIGN, "a and w must be 16-byte aligned");
+    CHECK(workspace == nullptr || aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
+    EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    ep.a_scale = a_scale;
+    ep.w_scale = w_scale;
+    ep.a_zero = a_zero;
+    ep.w_sum = w_sum;
+    if (workspace) {
+        ep.split_partial = (int32_t*)workspace;
+        ep.split_bytes = kSplitPartialBytes;
+    }
+    RUN(launch_gemm_i8(a, w, M, N, K, ep, S(stream)), "w8a8_linear_asym");
+    return DIT_OK;
+}
+
 int bf16_linear(const void* a, int64_t M, int64_t K, int64_t lda, const void* w, const float* bias,
                 int64_t N, void* y, int y_dtype, int64_t ldy, void* stream) {
     CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
@@ -615,6 +674,160 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     return DIT_OK;
 }
 
+struct GatedPlan {
+    size_t h, a8, sa, za, qkv, q, o, u, g, split, aq, total;
+};
+
+GatedPlan gated_plan(const dit_block_config* cfg, int64_t T, int64_t T_k) {
+    const size_t D = cfg->D, F = cfg->F;
+    GatedPlan p{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off += up256(bytes);
+        return at;
+    };
+    p.h = take(T * D * 2);
+    p.a8 = take(T * std::max(D, F));
+    p.sa = take(T * 4);
+    p.za = take(T * 4);
+    p.qkv = take(T * 3 * D * 2);   // only used when the fused QK epilogue is not available
+    p.q = take(T * D * 2);
+    p.o = take(T * D * 2);
+    p.u = take(T * F * 2);
+    p.g = take(T * F * 2);
+    p.split = take((size_t)kSplitPartialBytes);
+    p.aq = take(cfg->attn_quant ? attn_q8_layout(T, T_k, cfg->H).total : 0);
+    p.total = off;
+    return p;
+}
+
+int check_linear(const dit_linear& L, const char* name) {
+    CHECK(L.w != nullptr, DIT_E_NULL, "linear %s: w is NULL", name);
+    CHECK(aligned16(L.w), DIT_E_ALIGN, "linear %s: w must be 16-byte aligned", name);
+    if (L.s) CHECK(L.wsum && aligned16(L.wsum), DIT_E_NULL, "linear %s: int8 needs a 16-byte aligned wsum", name);
+    return DIT_OK;
+}
+
+int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, const dit_block_io* io,
+               uint8_t* ws, hipStream_t st) {
+    const int64_t T = io->T_q, D = cfg->D, F = cfg->F;
+    const int H = cfg->H;
+    const GatedPlan p = gated_plan(cfg, T, io->T_k);
+    const int64_t row_off = io->T_k - io->T_q;
+    const SegMap sm = make_segmap(io->seg_len, io->mod_of_seg, io->n_seg, row_off);
+    const AttnSegs segs = make_attn_segs(io->seg_len, io->n_seg);
+    const int64_t mstride = 6 * D;
+    void* x = io->x;
+    void* h = ws + p.h;
+    int8_t* a8 = (int8_t*)(ws + p.a8);
+    float* sa = (float*)(ws + p.sa);
+    int32_t* za = (int32_t*)(ws + p.za);
+    void* qb = ws + p.q;
+    void* ob = ws + p.o;
+    void* ub = ws + p.u;
+    void* gb = ws + p.g;
+    uint8_t* kc = (uint8_t*)io->k_cache + (size_t)row_off * D * 2;
+    uint8_t* vc = (uint8_t*)io->v_cache + (size_t)row_off * D * 2;
+    int32_t* split_partial = (int32_t*)(ws + p.split);
+    // one linear: int8 codes of the activation (already in a8/sa/za) if the
+    // linear is W8A8, else the bf16 activation A
+    auto lin = [&](const dit_linear& L, const void* A, int64_t N, int64_t K, const EpiParams& ep) -> hipError_t {
+        EpiParams e = ep;
+        if (!L.s) return launch_gemm_bf16(A, K, L.w, T, N, K, e, st);
+        e.a_scale = sa;
+        e.a_zero = za;
+        e.w_scale = L.s;
+        e.w_sum = L.wsum;
+        e.split_partial = split_partial;
+        e.split_bytes = kSplitPartialBytes;
+        return launch_gemm_i8(a8, (const int8_t*)L.w, T, N, K, e, st);
+    };
+    auto quant = [&](const void* A, int64_t K) -> hipError_t {
+        return launch_quantize_rows_asym(A, true, T, K, K, a8, sa, za, st);
+    };
+
+    {
+        ProfScope ps(DIT_SITE_ADALN1, st);
+        RUN(launch_adaln(x, true, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, nullptr,
+                         nullptr, st),
+            "adaln1");
+    }
+    if (w->qk.s || w->v.s) RUN(quant(h, D), "quantize h");
+    {
+        // Q/K: RMSNorm + RoPE in the GEMM epilogue (columns [0, D) q, [D, 2D) k)
+        EpiParams ep = store_epi(ws + p.qkv, 3 * D, true, w->qk.b);
+        ep.kind = EPI_QKV_ROPE;
+        ep.q_out = qb;
+        ep.k_out = kc;
+        ep.v_out = ob;   // unused columns of the unfused fallback land in o (overwritten by S4)
+        ep.g_q = w->g_q;
+        ep.g_k = w->g_k;
+        ep.cos_t = io->cos_t;
+        ep.sin_t = io->sin_t;
+        ep.qk_eps = cfg->qk_eps;
+        ep.D = D;
+        ProfScope ps(DIT_SITE_QKV_GEMM, st);
+        RUN(lin(w->qk, h, 2 * D, D, ep), "qk_gemm");
+        RUN(lin(w->v, h, D, D, store_epi(vc, D, true, w->v.b)), "v_gemm");
+    }
+    const float scale = 1.0f / std::sqrt(128.0f);
+    if (cfg->attn_quant) {
+        {
+            ProfScope ps(DIT_SITE_ATTN_QUANT, st);
+            RUN(launch_attn_quantize(qb, io->k_cache, io->v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st),
+                "attn_quantize");
+        }
+        ProfScope ps(DIT_SITE_ATTENTION, st);
+        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st), "attention_q8");
+    } else {
+        ProfScope ps(DIT_SITE_ATTENTION, st);
+        RUN(launch_attention_bf16(qb, io->k_cache, io->v_cache, ob, T, io->T_k, H, D, D, D, D, segs, scale, st),
+            "attention");
+    }
+    EpiParams resid{};
+    resid.kind = EPI_RESID;
+    resid.act_bf16 = 1;
+    resid.x = x;
+    resid.ldx = D;
+    resid.gate_stride = mstride;
+    resid.sm = sm;
+    {
+        if (w->o.s) RUN(quant(ob, D), "quantize o");
+        EpiParams ep = resid;
+        ep.bias = w->o.b;
+        ep.gate = io->mod + 2 * D;
+        ProfScope ps(DIT_SITE_OUT_GEMM, st);
+        RUN(lin(w->o, ob, D, D, ep), "out_gemm");
+    }
+    {
+        ProfScope ps(DIT_SITE_ADALN2, st);
+        RUN(launch_adaln(x, true, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, nullptr,
+                         nullptr, st),
+            "adaln2");
+    }
+    if (w->proj.s || w->gate.s) RUN(quant(h, D), "quantize h2");
+    {
+        // gated MLP: u = proj(h2) (bf16), then g = u * GELU(gate(h2)) in the gate GEMM's epilogue
+        ProfScope ps(DIT_SITE_UP_GEMM, st);
+        RUN(lin(w->proj, h, F, D, store_epi(ub, F, true, w->proj.b)), "proj_gemm");
+        EpiParams ep = store_epi(gb, F, true, w->gate.b);
+        ep.kind = EPI_GELU;
+        ep.gmul = ub;
+        ep.ldgm = F;
+        RUN(lin(w->gate, h, F, D, ep), "gate_gemm");
+    }
+    {
+        if (w->down.s) RUN(quant(gb, F), "quantize g");
+        EpiParams ep = resid;
+        ep.bias = w->down.b;
+        ep.gate = io->mod + 5 * D;
+        ProfScope ps(DIT_SITE_DOWN_GEMM, st);
+        RUN(lin(w->down, gb, D, F, ep), "down_gemm");
+    }
+    return DIT_OK;
+}
+
 }  // namespace
 
 size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k) {
@@ -664,6 +877,36 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
         if (s) return s;
     }
     return DIT_OK;
+}
+
+size_t dit_gated_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k) {
+    if (!cfg || T_q < 0 || T_k < T_q) return 0;
+    return gated_plan(cfg, T_q, T_k).total;
+}
+
+int dit_block_forward_gated(const dit_block_config* cfg, const dit_gated_block_weights* w, const dit_block_io* io,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_cfg(cfg);
+    if (s) return s;
+    CHECK(cfg->mode == DIT_MODE_BF16, DIT_E_DTYPE, "the gated block takes bf16 activations (mode BF16)");
+    CHECK(w != nullptr, DIT_E_NULL, "weights is NULL");
+    const dit_linear* all[6] = {&w->qk, &w->v, &w->o, &w->proj, &w->gate, &w->down};
+    const char* names[6] = {"qk", "v", "o", "proj", "gate", "down"};
+    for (int i = 0; i < 6; ++i) {
+        s = check_linear(*all[i], names[i]);
+        if (s) return s;
+    }
+    CHECK(w->g_q && w->g_k && aligned16(w->g_q) && aligned16(w->g_k), DIT_E_ALIGN,
+          "g_q and g_k must be non-NULL and 16-byte aligned");
+    CHECK(w->qk.b == nullptr || aligned16(w->qk.b), DIT_E_ALIGN, "qk bias must be 16-byte aligned");
+    s = check_io(cfg, io);
+    if (s) return s;
+    if (io->T_q == 0) return DIT_OK;
+    CHECK(aligned16(io->cos_t) && aligned16(io->sin_t), DIT_E_ALIGN, "cos_t and sin_t must be 16-byte aligned");
+    const size_t need = gated_plan(cfg, io->T_q, io->T_k).total;
+    CHECK(workspace != nullptr && workspace_bytes >= need, DIT_E_WORKSPACE, "workspace needs %zu bytes", need);
+    CHECK(aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
+    return gated_impl(cfg, w, io, (uint8_t*)workspace, S(stream));
 }
 
 size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k, int64_t N,

@@ -1,0 +1,129 @@
+// Pieces of the W8A8 recipe of "Qwen-Image-2.1 W8A8 - FlagOS for Mac"
+// (Quantization and validation): dynamic asymmetric per-token int8 activations
+// and the int8 weight column sums their zero points need.
+//
+// Asymmetric codes: the row's range widened to contain 0, lo = min(row, 0),
+// hi = max(row, 0); s = fp32(hi - lo) / 255; zero point z = -128 - rint(lo / s)
+// in [-128, 127]; q = clamp(rint(x / s) + z, -128, 127); IEEE fp32 divisions,
+// ties to even; an all-zero row gives s = 0, z = 0, q = 0.  A GEMM over such
+// codes subtracts z[m] * sum_k w[n, k] from its int32 sum.
+#include "common.h"
+#include "kernels.h"
+
+namespace dit {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+    if constexpr (std::is_same<T, __bf16>::value) {
+        const v8bf x = *reinterpret_cast<const v8bf*>(p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+    } else {
+        const v4f a = *reinterpret_cast<const v4f*>(p), b = *reinterpret_cast<const v4f*>(p + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = a[e];
+            v[4 + e] = b[e];
+        }
+    }
+}
+
+__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
+    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
+           ((uint32_t)(d & 0xFF) << 24);
+}
+
+__device__ __forceinline__ int asym_code(float x, float s, int z) {
+    if (s == 0.0f) return 0;
+    const int r = (int)rintf(__fdiv_rn(x, s)) + z;
+    return min(max(r, -128), 127);
+}
+
+// One workgroup per row; 8 consecutive values per thread and pass (K % 8 == 0).
+template <typename T>
+__global__ void __launch_bounds__(256) quant_asym_kernel(const T* __restrict__ x, int64_t ldx, int64_t K,
+                                                         int8_t* __restrict__ q, float* __restrict__ scale,
+                                                         int32_t* __restrict__ zero) {
+    __shared__ float red[2][4];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const T* xr = x + row * ldx;
+    float lo = 0.0f, hi = 0.0f;
+    for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
+        float v[8];
+        load8(xr + k, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo = fminf(lo, v[e]);
+            hi = fmaxf(hi, v[e]);
+        }
+    }
+    hi = wave_allmax(hi);
+    lo = -wave_allmax(-lo);
+    if (lane == 0) {
+        red[0][wave] = lo;
+        red[1][wave] = hi;
+    }
+    __syncthreads();
+    lo = fminf(fminf(red[0][0], red[0][1]), fminf(red[0][2], red[0][3]));
+    hi = fmaxf(fmaxf(red[1][0], red[1][1]), fmaxf(red[1][2], red[1][3]));
+    const float s = __fdiv_rn(hi - lo, 255.0f);
+    const int z = s == 0.0f ? 0 : min(max(-128 - (int)rintf(__fdiv_rn(lo, s)), -128), 127);
+    int8_t* qr = q + row * K;
+    for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
+        float v[8];
+        load8(xr + k, v);
+        uint2 o;
+        o.x = pack4(asym_code(v[0], s, z), asym_code(v[1], s, z), asym_code(v[2], s, z), asym_code(v[3], s, z));
+        o.y = pack4(asym_code(v[4], s, z), asym_code(v[5], s, z), asym_code(v[6], s, z), asym_code(v[7], s, z));
+        *reinterpret_cast<uint2*>(qr + k) = o;
+    }
+    if (tid == 0) {
+        scale[row] = s;
+        zero[row] = z;
+    }
+}
+
+// One wave per weight row: out[n] = sum_k w[n, k] (K % 16 == 0).
+__global__ void __launch_bounds__(256) int8_colsum_kernel(const int8_t* __restrict__ w, int64_t N, int64_t K,
+                                                          int32_t* __restrict__ out) {
+    const int64_t n = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (n >= N) return;
+    const int8_t* wr = w + n * K;
+    int acc = 0;
+    for (int64_t k = (int64_t)lane * 16; k < K; k += kWave * 16) {
+        const v4i c = *reinterpret_cast<const v4i*>(wr + k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int x = c[e];
+            acc += (int)(int8_t)(x & 0xFF) + (int)(int8_t)((x >> 8) & 0xFF) + (int)(int8_t)((x >> 16) & 0xFF) +
+                   (int)(int8_t)((x >> 24) & 0xFF);
+        }
+    }
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) acc += __shfl_xor(acc, m, kWave);
+    if (lane == 0) out[n] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_rows_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                     float* scale, int32_t* zero, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (bf16)
+        quant_asym_kernel<__bf16><<<(unsigned)M, 256, 0, st>>>((const __bf16*)x, ldx, K, q, scale, zero);
+    else
+        quant_asym_kernel<float><<<(unsigned)M, 256, 0, st>>>((const float*)x, ldx, K, q, scale, zero);
+    return hipGetLastError();
+}
+
+hipError_t launch_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t st) {
+    if (N == 0) return hipSuccess;
+    int8_colsum_kernel<<<(unsigned)((N + 3) / 4), 256, 0, st>>>(w, N, K, out);
+    return hipGetLastError();
+}
+
+}  // namespace dit

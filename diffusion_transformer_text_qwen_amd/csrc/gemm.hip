@@ -115,7 +115,8 @@ __device__ __forceinline__ void epilogue(const EpiParams& ep, int64_t m, int64_t
         if constexpr (EV == EV_STORE_ACC) ep.acc_out[m * ep.ldacc + n] = acc_i;
     } else if constexpr (EV == EV_GELU) {
         const float u = rb ? bf16r(v) : v;
-        const float g = gelu_tanh(u);
+        float g = gelu_tanh(u);
+        if (ep.gmul) g *= (float)reinterpret_cast<const __bf16*>(ep.gmul)[m * ep.ldgm + n];
         if (ep.y_bf16)
             reinterpret_cast<__bf16*>(ep.y)[m * ep.ldy + n] = to_bf16(g);
         else
@@ -151,6 +152,16 @@ __device__ __forceinline__ void epilogue16(const EpiParams& ep, int64_t m, int64
         if constexpr (EV == EV_GELU) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = gelu_tanh(rb ? bf16r(v[e]) : v[e]);
+            if (ep.gmul) {
+                const v8bf* up = reinterpret_cast<const v8bf*>(reinterpret_cast<const __bf16*>(ep.gmul) +
+                                                               m * ep.ldgm + n0);
+                const v8bf u0 = up[0], u1 = up[1];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[e] *= (float)u0[e];
+                    v[8 + e] *= (float)u1[e];
+                }
+            }
         }
         if (ep.y_bf16) {
             v8bf o0, o1;
@@ -312,7 +323,7 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
                 const int64_t n = n0 + wn * 64 + j * 16 + lane % 16;
                 if (m < M && n < N) {
                     if constexpr (I8) {
-                        const int32_t a = acc[i][j][r];
+                        const int32_t a = acc[i][j][r] - (ep.a_zero ? ep.a_zero[m] * ep.w_sum[n] : 0);
                         const float v = (float)a * ep.a_scale[m] * ep.w_scale[n];
                         epilogue<EV>(ep, m, n, v, a);
                     } else {
@@ -605,10 +616,16 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             if (ok) {
                 if constexpr (I8) {
                     const float sa = rows_sa[i][pass];
+                    const int za = ep.a_zero ? ep.a_zero[m] : 0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const v4i t = *reinterpret_cast<const v4i*>(
+                        v4i t = *reinterpret_cast<const v4i*>(
                             reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                        if (ep.a_zero) {
+                            const v4i ws = *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) t[e] -= za * ws[e];
+                        }
                         if constexpr (EV == EV_QKV) {
                             const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
 #pragma unroll
@@ -776,6 +793,11 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+        if (ep.a_zero) {
+            const int za = ep.a_zero[m];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) sum[q] -= za * *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
+        }
         const float sa = ep.a_scale[m];
         float v[16];
 #pragma unroll
@@ -794,6 +816,11 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     for (int s2 = 0; s2 < S; ++s2)
 #pragma unroll
         for (int q = 0; q < 4; ++q) sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+    if (ep.a_zero) {
+        const int za = ep.a_zero[m];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sum[q] -= za * *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
+    }
     const float sa = ep.a_scale[m];
     float v[16];
     int32_t ai[16];

@@ -49,6 +49,14 @@ struct EpiParams {
     const float* sin_t;
     float qk_eps;
     int64_t D;
+    // Asymmetric int8 activations (NULL = symmetric): the int32 sum becomes
+    // acc - a_zero[m] * w_sum[n] before scaling.
+    const int32_t* a_zero;
+    const int32_t* w_sum;
+    // EPI_GELU only (NULL = none): multiply GELU(v) by this bf16 [M, ldgm]
+    // tensor (the gated MLP's proj output).
+    const void* gmul;
+    int64_t ldgm;
 };
 
 // Bytes of split scratch the int8 GEMM may use for any shape: at most C tiles x
@@ -64,6 +72,9 @@ hipError_t launch_gemm_f32(const float* a, int64_t lda, const float* w, int64_t 
 
 hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, float* scale, hipStream_t st);
+hipError_t launch_quantize_rows_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                                     float* scale, int32_t* zero, hipStream_t st);
+hipError_t launch_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t st);
 hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
                                      hipStream_t st);
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,

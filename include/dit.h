@@ -90,6 +90,34 @@ int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * Asymmetric per-row int8 quantization ("Qwen-Image-2.1 W8A8 - FlagOS for Mac",
+ * Quantization and validation: dynamic asymmetric INT8 activations per token,
+ * fp32 scales).  The page gives no formula; reading: the row's range widened to
+ * contain 0, lo = min(row, 0), hi = max(row, 0); scale = fp32(hi - lo) / 255,
+ * zero point z = -128 - rint(lo / scale) (in [-128, 127]),
+ * q = clamp(rint(x / scale) + z, -128, 127), IEEE fp32 divisions, ties to even;
+ * a code stands for (q - z) * scale; an all-zero row gives scale 0, z 0, q 0.
+ * x [M, K] bf16|f32 (row stride ldx); q [M, K] int8 (row stride K); scale [M]
+ * fp32; zero [M] int32.  Supported: K % 8 == 0, ldx % 8 == 0, 16-byte aligned x, q.
+ */
+int dit_quantize_rows_asym(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx, int8_t* q,
+                           float* scale, int32_t* zero, void* stream);
+
+/* out[n] = sum_k w[n, k] for int8 w [N, K] (row stride K): the row sums a GEMM
+ * over zero-point activation codes subtracts (z[m] * out[n]).  K % 16 == 0. */
+int dit_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, void* stream);
+
+/*
+ * w8a8_linear over asymmetric activation codes (dit_quantize_rows_asym):
+ *   y[m, n] = float(sum_k a[m,k] w[n,k] - a_zero[m] * w_sum[n]) * a_scale[m] * w_scale[n] + bias[n]
+ * with w_sum from dit_int8_colsum (16-byte aligned).  a_zero == NULL is
+ * w8a8_linear.  Supported as w8a8_linear, with K <= 65536 (255*127*K < 2^31).
+ */
+int w8a8_linear_asym(const int8_t* a, const float* a_scale, const int32_t* a_zero, int64_t M, int64_t K,
+                     const int8_t* w, const float* w_scale, const int32_t* w_sum, const float* bias, int64_t N,
+                     void* y, int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * bf16 linear for the non-quantized linears: y = a w^T + bias with fp32
  * accumulation.  a [M, K] bf16 (row stride lda), w [N, K] bf16 (row stride K),
  * bias [N] fp32 or NULL, y [M, N] bf16 or fp32 (row stride ldy).
@@ -289,6 +317,51 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
                       int32_t n_blocks, const dit_block_io* io, void* const* k_caches,
                       void* const* v_caches, void* workspace, size_t workspace_bytes,
                       void* stream);
+
+/* ------------------------------------------------------------------ gated-MLP block, per-linear W8A8 */
+
+/*
+ * One linear of the gated block ("Qwen-Image-2.1 W8A8 - FlagOS for Mac",
+ * Quantization and validation: a mixed W8A8/BF16 transformer in which only some
+ * linears run W8A8).  s != NULL: w holds int8 codes [N, K] (symmetric per
+ * output channel, scales s [N]) and wsum [N] their row sums (dit_int8_colsum);
+ * the activation is quantized asymmetrically per token (dit_quantize_rows_asym).
+ * s == NULL: w is bf16 [N, K] and wsum is ignored.  b: fp32 bias [N] or NULL.
+ */
+typedef struct {
+    const void* w;
+    const float* s;
+    const int32_t* wsum;
+    const float* b;
+} dit_linear;
+
+/*
+ * Weights of the gated-MLP block.  The page names Q/K and MLP proj/gate
+ * modules, and its checkpoint size implies a gated MLP; reading of the MLP:
+ *   u = h2 W_proj^T + b_proj;  t = h2 W_gate^T + b_gate  (each stored bf16)
+ *   g = u * GELU_tanh(t)  (stored bf16);  y2 = g W_down^T + b_down
+ * qk [2D, D] (q rows, then k rows), v [D, D], o [D, D], proj/gate [F, D],
+ * down [D, F]; g_q, g_k [128] fp32 (16-byte aligned).
+ */
+typedef struct {
+    dit_linear qk, v, o, proj, gate, down;
+    const float *g_q, *g_k;
+} dit_gated_block_weights;
+
+/* Workspace of dit_block_forward_gated (bytes). */
+size_t dit_gated_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k);
+
+/*
+ * The block of dit_block_forward with the gated MLP above and a per-linear
+ * choice of W8A8 (the page's recipe: Q/K, proj and gate W8A8 in blocks 2..29
+ * of 32, zero-based, everything else bf16; the caller picks per block by
+ * passing int8 or bf16 weights).  cfg->mode must be DIT_MODE_BF16 (bf16
+ * activations); cfg->F is the gated width; cfg->attn_quant selects the
+ * int8/fp8 attention.  io as for dit_block_forward (cos_t, sin_t 16-byte
+ * aligned).  Errors before any launch as dit_block_forward.
+ */
+int dit_block_forward_gated(const dit_block_config* cfg, const dit_gated_block_weights* w, const dit_block_io* io,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------ one velocity evaluation */
 

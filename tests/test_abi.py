@@ -232,3 +232,36 @@ def test_attn_q8_validation():
     assert lib.block_causal_attention_q8(q, 0, 20, 1, None, 128, sp, 2, 0.0, S) == 0        # T_q == 0: no-op
     cfg = dq.BlockConfig(dq.MODE_F32, 512, 4, 128, 2048, 1e-6, 1e-6, 1)
     assert lib.dit_block_workspace_bytes(ctypes.byref(cfg), 96, 96) > 0
+
+
+def test_gated_validation():
+    """Asymmetric quantization, column sums, the zero-point linear and the gated
+    block reject bad arguments before any HIP call."""
+    lib = dq.lib()
+    p = 256
+    assert lib.dit_quantize_rows_asym(p, 9, 4, 64, 64, p, p, p, S) == 3              # dtype
+    assert lib.dit_quantize_rows_asym(p, 1, 4, 60, 64, p, p, p, S) == 5              # K % 8
+    assert lib.dit_quantize_rows_asym(p, 1, 4, 64, 64, p, p, None, S) == 1           # zero NULL
+    assert lib.dit_quantize_rows_asym(p, 1, 0, 64, 64, None, None, None, S) == 0     # M == 0: no-op
+    assert lib.dit_int8_colsum(p, 8, 40, p, S) == 5                                  # K % 16
+    assert lib.dit_int8_colsum(264, 8, 64, p, S) == 4                                # misaligned w
+    assert lib.w8a8_linear_asym(p, p, p, 4, 128, p, p, None, None, 16, p, 1, 16, None, 0, S) == 1   # no w_sum
+    assert lib.w8a8_linear_asym(p, p, p, 4, 128 * 1024, p, p, p, None, 16, p, 1, 16, None, 0, S) == 5  # K bound
+    cfg = dq.BlockConfig(dq.MODE_W8A8, 512, 4, 128, 1536, 1e-6, 1e-6, 0)
+    lin = dq.LinearC(w=p, s=None, wsum=None, b=p)
+    w = dq.GatedBlockWeightsC(qk=lin, v=lin, o=lin, proj=lin, gate=lin, down=lin, g_q=p, g_k=p)
+    segs = (ctypes.c_int32 * 2)(24, 64)
+    mos = (ctypes.c_int32 * 2)(0, 0)
+    io = dq.BlockIO(x=p, mod=p, n_mod=1, mod_of_seg=ctypes.cast(mos, ctypes.c_void_p), cos_t=p, sin_t=p,
+                    seg_len=ctypes.cast(segs, ctypes.c_void_p), n_seg=2, T_q=88, T_k=88, k_cache=p, v_cache=p)
+    call = lambda c, ww, wsb=1 << 40: lib.dit_block_forward_gated(ctypes.byref(c), ctypes.byref(ww), ctypes.byref(io),
+                                                                 p, wsb, S)
+    assert call(cfg, w) == 3                                       # activations must be bf16 (mode BF16)
+    cfg.mode = dq.MODE_BF16
+    w.proj = dq.LinearC(w=p, s=p, wsum=None, b=p)
+    assert call(cfg, w) == 1                                       # int8 linear without its row sums
+    w.proj = dq.LinearC(w=264, s=None, wsum=None, b=p)
+    assert call(cfg, w) == 4                                       # misaligned weights
+    w.proj = lin
+    assert call(cfg, w, wsb=64) == 6                               # workspace too small
+    assert lib.dit_gated_block_workspace_bytes(ctypes.byref(cfg), 88, 88) > 0
