@@ -15,6 +15,10 @@ workload, [256 text | 1024 reference | 16384 target], uncached step (17,664
 rows) and the cached step that reuses the prefix K/V (16,384 rows), the latter
 also with the int8/fp8 attention.
 
+Also measured (reported under "gated_recipe_1024px"): one gated-MLP block
+(F 12288) over the same tokens, all-bf16 and with the FlagOS page's W8A8 scope
+(Q/K, proj and gate int8 with asymmetric per-token activations).
+
 Also measured (reported under "attn_int8_fp8_1024px"): the same step as the
 timed one with the int8 Q K^T / fp8 P V attention (the pages' later denoising
 steps), and the 40-step loop with the first 7 steps bf16 attention, the rest
@@ -331,6 +335,49 @@ def run_edit(args, dq, torch, ditsynth, reps):
     return res
 
 
+def run_gated(args, dq, torch, ditsynth, reps):
+    """One gated-MLP block (F = 12288) over the 1024^2 token layout: all linears
+    bf16, and the FlagOS page's W8A8 scope (Q/K, proj, gate int8 with asymmetric
+    per-token activations; V, out, down bf16)."""
+    w = ditsynth.workload(3)
+    D, H, T, F = w.D, w.H, w.T, 12288
+    dev = "cuda"
+    arrays = ditsynth.device_gated_block_weights(w, 0, F, dev)
+    si = ditsynth.device_step_inputs(w, dev)
+    x0 = torch.randn((T, D), generator=ditsynth.device_generator(w, 3000), device=dev).to(torch.bfloat16)
+    cos = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    sin = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    dq.rope_tables(w.text, w.images, 0, T, cos, sin)
+    kc = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+    vc = torch.empty_like(kc)
+    x = torch.empty_like(x0)
+    mod = si["mod"][0:1].contiguous()
+    res = {"rows": T, "F": F}
+    for label, int8, aq in (("bf16", (), False), ("recipe_w8a8", ("qk", "proj", "gate"), False),
+                            ("recipe_w8a8_attn_int8_fp8", ("qk", "proj", "gate"), True)):
+        cfg = dq.block_config("bf16", D, H, F, attn_quant=aq)
+        gw = dq.GatedBlockWeights(arrays, int8)
+        ws = torch.empty(dq.gated_workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
+
+        def call():
+            x.copy_(x0)
+            dq.block_forward_gated(cfg, gw, x, mod, [0] * len(w.seg_len), cos, sin, w.seg_len, kc, vc, ws)
+        call()
+        torch.cuda.synchronize()
+        dq.profile_begin(reps * 16 + 4)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        prof = dq.profile_end()
+        blk_ms = sum(p["ms"] for p in prof.values()) / reps
+        res[label] = {"block_ms": round(blk_ms, 3), "block_tokens_per_s": round(T / (blk_ms * 1e-3), 1),
+                      "finite": bool(torch.isfinite(x.float()).all().item()),
+                      "sites_us": {k: round(p["ms"] / reps * 1e3, 1) for k, p in prof.items() if p["count"]}}
+        del gw, ws
+    log(f"gated block: {res}")
+    return res
+
+
 def cpu_baseline(ditsynth):
     """The oracle, untuned, on one block of the 32-block stack (all 4352 rows) on the host."""
     import numpy as np
@@ -429,6 +476,7 @@ def main():
         line["denoise_loop_1024px"] = loop
     if not args.no_edit:
         line["edit_2048px"] = run_edit(args, dq, torch, ditsynth, args.edit_reps)
+        line["gated_recipe_1024px"] = run_gated(args, dq, torch, ditsynth, args.edit_reps)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one block ...")
         line["cpu_baseline"] = cpu_baseline(ditsynth)

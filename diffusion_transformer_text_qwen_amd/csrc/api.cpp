@@ -753,7 +753,10 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
                          nullptr, st),
             "adaln1");
     }
-    if (w->qk.s || w->v.s) RUN(quant(h, D), "quantize h");
+    if (w->qk.s || w->v.s) {
+        ProfScope ps(DIT_SITE_ADALN1, st);
+        RUN(quant(h, D), "quantize h");
+    }
     {
         // Q/K: RMSNorm + RoPE in the GEMM epilogue (columns [0, D) q, [D, 2D) k)
         EpiParams ep = store_epi(ws + p.qkv, 3 * D, true, w->qk.b);
@@ -793,7 +796,10 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     resid.gate_stride = mstride;
     resid.sm = sm;
     {
-        if (w->o.s) RUN(quant(ob, D), "quantize o");
+        if (w->o.s) {
+            ProfScope pq(DIT_SITE_QUANT_O, st);
+            RUN(quant(ob, D), "quantize o");
+        }
         EpiParams ep = resid;
         ep.bias = w->o.b;
         ep.gate = io->mod + 2 * D;
@@ -806,7 +812,10 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
                          nullptr, st),
             "adaln2");
     }
-    if (w->proj.s || w->gate.s) RUN(quant(h, D), "quantize h2");
+    if (w->proj.s || w->gate.s) {
+        ProfScope ps(DIT_SITE_ADALN2, st);
+        RUN(quant(h, D), "quantize h2");
+    }
     {
         // gated MLP: u = proj(h2) (bf16), then g = u * GELU(gate(h2)) in the gate GEMM's epilogue
         ProfScope ps(DIT_SITE_UP_GEMM, st);
@@ -818,7 +827,10 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
         RUN(lin(w->gate, h, F, D, ep), "gate_gemm");
     }
     {
-        if (w->down.s) RUN(quant(gb, F), "quantize g");
+        if (w->down.s) {
+            ProfScope pq(DIT_SITE_QUANT_G, st);
+            RUN(quant(gb, F), "quantize g");
+        }
         EpiParams ep = resid;
         ep.bias = w->down.b;
         ep.gate = io->mod + 5 * D;

@@ -335,6 +335,22 @@ def device_generator(w: Workload, stream: int, device="cuda"):
     return g
 
 
+def device_gated_block_weights(w: Workload, block: int, F: int, device="cuda"):
+    """Device draws of gated_block_weights (width F), every tensor on the bf16 grid."""
+    g = device_generator(w, 2000 + block, device)
+    D = w.D
+    out = {}
+    for name, shape in (("w_qk", (2 * D, D)), ("b_qk", (2 * D,)), ("w_v", (D, D)), ("b_v", (D,)),
+                        ("g_q", (HEAD_DIM,)), ("g_k", (HEAD_DIM,)), ("w_o", (D, D)), ("b_o", (D,)),
+                        ("w_proj", (F, D)), ("b_proj", (F,)), ("w_gate", (F, D)), ("b_gate", (F,)),
+                        ("w_down", (D, F)), ("b_down", (D,))):
+        t = device_normal(shape, 0.02, g, device)
+        if name.startswith("g_"):
+            t = t + 1.0
+        out[name] = t.to(_torch().bfloat16).to(_torch().float32)
+    return out
+
+
 def device_block_weights(w: Workload, block: int, device="cuda"):
     """Yields (name, fp32 device tensor) for one block, masters first (see block_weights)."""
     g = device_generator(w, 1000 + block, device)
