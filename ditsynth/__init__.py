@@ -162,6 +162,17 @@ def gated_block_weights(w: Workload, block: int = 0) -> Dict[str, np.ndarray]:
     return out
 
 
+def mxfp4_weights(N: int, K: int, seed: int, scale_exp: int = 121):
+    """A synthetic MXFP4 checkpoint matrix [N, K]: uniform random 4-bit E2M1 codes
+    packed two per byte ([N, K/2] uint8) and E8M0 group scales ([N, K/32] uint8)
+    drawn around 2^(scale_exp - 127) (x2^-1..x2^1), so weights have magnitudes
+    near those of the N(0, 0.02) draws.  Codes are drawn directly: no encoder."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = (scale_exp + rng.integers(-1, 2, (N, K // 32))).astype(np.uint8)
+    return codes, scales
+
+
 def _modulation_sets(w: Workload, n_sets: int, rows: int = 6) -> np.ndarray:
     """[n_sets, rows, D] modulation rows, each set from its own timestep embedding."""
     rng = _streams(w, _S_BLOCK0)[_S_MOD]

@@ -33,7 +33,8 @@ __all__ = [
     "ROPE_AXES", "ROPE_THETA", "LN_EPS", "QK_EPS",
     "round_fp8_e4m3", "encode_fp8_e4m3", "decode_fp8_e4m3", "quantize_attn_q", "quantize_attn_k",
     "quantize_attn_v", "attention_q8", "attention_q8_bound", "attention_quantized", "ATTN_KEY_TILE", "FP8_MAX",
-    "quantize_rows_asym", "w8a8_linear_asym", "block_forward_gated", "GATED_LINEARS",
+    "quantize_rows_asym", "w8a8_linear_asym", "block_forward_gated", "GATED_LINEARS", "mxfp4_decode",
+    "E2M1_VALUES",
 ]
 
 HEAD_DIM = 128
@@ -149,6 +150,35 @@ def w8a8_linear_asym(qa, sa, za, qw, sw, bias) -> np.ndarray:
     if bias is not None:
         y = y + np.asarray(bias, np.float64)[None, :]
     return y
+
+
+# [Paiton, What was quantized]: MXFP4 storage, E2M1 values packed low nibble
+# first, one E8M0 scale per group of 32 input columns.  E2M1 (OCP MX): sign,
+# 2 exponent bits (bias 1), 1 mantissa bit -> 0, 0.5, 1, 1.5, 2, 3, 4, 6; E8M0:
+# the power of two 2^(e - 127) (e = 255 is NaN).
+E2M1_VALUES = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def mxfp4_decode(codes, scales) -> np.ndarray:
+    """Weights [N, K] (fp64) from packed codes [N, K/2] (uint8, element 2i in the
+    low nibble of byte i) and E8M0 scales [N, K/32] (uint8).  [Paiton, Runtime
+    precision and quality / What was quantized]: the runtime reconstructs these
+    weights and computes in bf16; every E2M1 value times a power of two is
+    exact in bf16 inside bf16's exponent range."""
+    codes = np.asarray(codes, np.uint8)
+    scales = np.asarray(scales, np.uint8)
+    N, half = codes.shape
+    K = 2 * half
+    if scales.shape != (N, K // 32):
+        raise ValueError("mxfp4_decode: scales must be [N, K/32]")
+    nib = np.empty((N, K), np.uint8)
+    nib[:, 0::2] = codes & 0x0F
+    nib[:, 1::2] = codes >> 4
+    mag = np.asarray(E2M1_VALUES, np.float64)[nib & 7]
+    val = np.where(nib & 8, -mag, mag)
+    e = scales.astype(np.int64)
+    pw = np.where(e == 255, np.nan, np.ldexp(1.0, e - 127))
+    return val * np.repeat(pw, 32, axis=1)
 
 
 def w8a8_linear(qa, sa, qw, sw, bias) -> np.ndarray:
@@ -549,7 +579,7 @@ GATED_LINEARS = ("w_qk", "w_v", "w_o", "w_proj", "w_gate", "w_down")
 
 def block_forward_gated(x, mod, mod_of_seg, seg_len, cos, sin, weights, int8=(), attn_quant: bool = False,
                         k_prefix=None, v_prefix=None, ln_eps: float = LN_EPS,
-                        qk_eps: float = QK_EPS) -> Dict[str, np.ndarray]:
+                        qk_eps: float = QK_EPS, mx=None) -> Dict[str, np.ndarray]:
     """The block with a gated MLP and a per-linear choice of W8A8 ([FlagOS,
     Quantization and validation]: Q/K and the MLP proj/gate linears of the middle
     blocks run W8A8 with asymmetric per-token activations, the rest bf16).
@@ -558,8 +588,10 @@ def block_forward_gated(x, mod, mod_of_seg, seg_len, cos, sin, weights, int8=(),
     w_proj [F, D], w_gate [F, D], w_down [D, F] (fp32 masters on the bf16 grid),
     their biases b_*, and g_q, g_k.  int8: names of the linears that run W8A8
     (weights quantized symmetric per output channel, activations asymmetric per
-    token, w8a8_linear_asym); every other linear is bf16.  bf16 storage
-    semantics throughout (mode "bf16").
+    token, w8a8_linear_asym); mx: {name: (codes, scales)} for linears stored as
+    MXFP4 ([Paiton]: reconstructed weights, bf16 arithmetic; the reconstruction
+    rounded to bf16 is exact in range); every other linear is bf16.  bf16
+    storage semantics throughout (mode "bf16").
 
     Reading for the MLP (the page names a proj and a gate module; the other
     block structure of block_forward is kept):
@@ -567,6 +599,7 @@ def block_forward_gated(x, mod, mod_of_seg, seg_len, cos, sin, weights, int8=(),
       g = u * GELU_tanh(t)  (stored bf16);  y2 = g W_down^T + b_down
     """
     mode = "bf16"
+    mx = mx or {}
     x = np.asarray(x, np.float64)
     T_q, D = x.shape
     H = D // HEAD_DIM
@@ -575,6 +608,9 @@ def block_forward_gated(x, mod, mod_of_seg, seg_len, cos, sin, weights, int8=(),
 
     def lin(a, name):
         b = weights["b" + name[1:]]
+        if name in mx:
+            codes, scales = mx[name]
+            return linear(a, round_bf16(mxfp4_decode(codes, scales)), b)
         if name in int8:
             qa, sa, za = quantize_rows_asym(a)
             qw, sw = quantize_rows(weights[name])
