@@ -43,7 +43,7 @@ class BlockWeightsC(ctypes.Structure):
 
 
 class LinearC(ctypes.Structure):
-    _fields_ = [("w", _vp), ("s", _vp), ("wsum", _vp), ("b", _vp)]
+    _fields_ = [("w", _vp), ("s", _vp), ("wsum", _vp), ("b", _vp), ("mx_scale", _vp)]
 
 
 class GatedBlockWeightsC(ctypes.Structure):
@@ -85,6 +85,10 @@ _SIGS = {
     "dit_int8_colsum": ([_vp, _c_i64, _c_i64, _vp, _vp], ctypes.c_int),
     "w8a8_linear_asym": ([_vp, _vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64,
                           _vp, ctypes.c_size_t, _vp], ctypes.c_int),
+    "dit_mxfp4_expand": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp], ctypes.c_int),
+    "mxfp4_linear_workspace_bytes": ([_c_i64, _c_i64], ctypes.c_size_t),
+    "mxfp4_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp,
+                      ctypes.c_size_t, _vp], ctypes.c_int),
     "dit_gated_block_workspace_bytes": ([ctypes.POINTER(BlockConfig), _c_i64, _c_i64], ctypes.c_size_t),
     "dit_block_forward_gated": ([ctypes.POINTER(BlockConfig), ctypes.POINTER(GatedBlockWeightsC),
                                  ctypes.POINTER(BlockIO), _vp, ctypes.c_size_t, _vp], ctypes.c_int),
@@ -188,6 +192,20 @@ def w8a8_linear_asym(a, a_scale, a_zero, w, w_scale, w_sum, bias, y, workspace=N
     _check(lib().w8a8_linear_asym(_p(a), _p(a_scale), _p(a_zero), M, K, _p(w), _p(w_scale), _p(w_sum), _p(bias), N,
                                   _p(y), _dt(y), y.stride(0), _p(workspace), wsb, _stream(stream)),
            "w8a8_linear_asym")
+
+
+def mxfp4_expand(codes, scales, w_bf16, stream=None) -> None:
+    """MXFP4 codes [N, K/2] uint8 + E8M0 scales [N, K/32] uint8 -> w_bf16 [N, K]."""
+    N, K = w_bf16.shape
+    _check(lib().dit_mxfp4_expand(_p(codes), _p(scales), N, K, _p(w_bf16), _stream(stream)), "dit_mxfp4_expand")
+
+
+def mxfp4_linear(a, codes, scales, bias, y, workspace, stream=None) -> None:
+    M, K = a.shape
+    N = codes.shape[0]
+    _check(lib().mxfp4_linear(_p(a), M, K, a.stride(0), _p(codes), _p(scales), _p(bias), N, _p(y), _dt(y),
+                              y.stride(0), _p(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)), "mxfp4_linear")
 
 
 def w8a8_linear_workspace_bytes() -> int:
@@ -446,16 +464,23 @@ class GatedBlockWeights:
     """Device weights of one gated block: arrays w_qk, w_v, w_o, w_proj, w_gate,
     w_down ([N, K]) with biases b_* and gains g_q, g_k; the linears named in
     ``int8`` are quantized per output channel on the GPU (codes, scales and the
-    codes' row sums), the others uploaded as bf16."""
+    codes' row sums); ``mx`` maps linears to MXFP4 (codes [N, K/2], E8M0 scales
+    [N, K/32]) uploaded as they are; the others uploaded as bf16."""
 
-    def __init__(self, arrays: Dict, int8: Sequence[str] = (), device="cuda"):
+    def __init__(self, arrays: Dict, int8: Sequence[str] = (), device="cuda", mx: Optional[Dict] = None):
         self.t: Dict[str, torch.Tensor] = {}
         self.int8 = tuple(int8)
+        mx = mx or {}
         lin = {}
         for name in GATED_LINEARS:
-            a = torch.as_tensor(arrays["w_" + name])
             b = torch.as_tensor(arrays["b_" + name]).to(device=device, dtype=torch.float32).contiguous()
             self.t["b_" + name] = b
+            if name in mx:
+                codes, scales = (torch.as_tensor(v).to(device=device, dtype=torch.uint8).contiguous() for v in mx[name])
+                self.t.update({"mx_" + name: codes, "mxs_" + name: scales})
+                lin[name] = LinearC(w=_p(codes), s=None, wsum=None, b=_p(b), mx_scale=_p(scales))
+                continue
+            a = torch.as_tensor(arrays["w_" + name])
             if name in self.int8:
                 master = a.to(device=device, dtype=torch.float32).contiguous()
                 q = torch.empty(master.shape, dtype=torch.int8, device=device)

@@ -210,6 +210,42 @@ int dit_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, void* s
     return DIT_OK;
 }
 
+int dit_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* w_bf16,
+                     void* stream) {
+    CHECK(N >= 0 && K >= 1, DIT_E_SHAPE, "need N>=0, K>=1");
+    CHECK(K % 32 == 0, DIT_E_UNSUPPORTED, "K must be a multiple of 32");
+    CHECK(N * (K / 32) < ((int64_t)1 << 31) * 256, DIT_E_UNSUPPORTED, "too many groups");
+    if (N == 0) return DIT_OK;
+    CHECK(codes && scales && w_bf16, DIT_E_NULL, "codes, scales and w_bf16 must be non-NULL");
+    CHECK(aligned16(codes) && aligned16(w_bf16), DIT_E_ALIGN, "codes and w_bf16 must be 16-byte aligned");
+    RUN(launch_mxfp4_expand(codes, scales, N, K, w_bf16, S(stream)), "mxfp4_expand");
+    return DIT_OK;
+}
+
+size_t mxfp4_linear_workspace_bytes(int64_t N, int64_t K) {
+    return (N < 0 || K < 0) ? 0 : (size_t)N * (size_t)K * 2;
+}
+
+int mxfp4_linear(const void* a, int64_t M, int64_t K, int64_t lda, const uint8_t* codes, const uint8_t* scales,
+                 const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
+    CHECK(M >= 0 && K >= 1 && N >= 1 && lda >= K && ldy >= N, DIT_E_SHAPE, "bad sizes or strides");
+    CHECK(K % 64 == 0 && lda % 8 == 0, DIT_E_UNSUPPORTED, "K must be a multiple of 64, lda of 8");
+    CHECK(N % 16 == 0, DIT_E_UNSUPPORTED, "N must be a multiple of 16");
+    CHECK(workspace != nullptr && workspace_bytes >= mxfp4_linear_workspace_bytes(N, K), DIT_E_WORKSPACE,
+          "workspace needs %zu bytes", mxfp4_linear_workspace_bytes(N, K));
+    if (M == 0) return DIT_OK;
+    CHECK(a && codes && scales && y, DIT_E_NULL, "a, codes, scales and y must be non-NULL");
+    CHECK(aligned16(a) && aligned16(codes) && aligned16(workspace), DIT_E_ALIGN,
+          "a, codes and workspace must be 16-byte aligned");
+    hipStream_t st = S(stream);
+    RUN(launch_mxfp4_expand(codes, scales, N, K, workspace, st), "mxfp4_expand");
+    EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    RUN(launch_gemm_bf16(a, lda, workspace, M, N, K, ep, st), "mxfp4_linear");
+    return DIT_OK;
+}
+
 int w8a8_linear_asym(const int8_t* a, const float* a_scale, const int32_t* a_zero, int64_t M, int64_t K,
                      const int8_t* w, const float* w_scale, const int32_t* w_sum, const float* bias, int64_t N,
                      void* y, int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream) {
@@ -675,7 +711,7 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
 }
 
 struct GatedPlan {
-    size_t h, a8, sa, za, qkv, q, o, u, g, split, aq, total;
+    size_t h, a8, sa, za, qkv, q, o, u, g, split, aq, wx, total;
 };
 
 GatedPlan gated_plan(const dit_block_config* cfg, int64_t T, int64_t T_k) {
@@ -698,6 +734,7 @@ GatedPlan gated_plan(const dit_block_config* cfg, int64_t T, int64_t T_k) {
     p.g = take(T * F * 2);
     p.split = take((size_t)kSplitPartialBytes);
     p.aq = take(cfg->attn_quant ? attn_q8_layout(T, T_k, cfg->H).total : 0);
+    p.wx = take(std::max(2 * D * D, F * D) * 2);   // MXFP4 weights expanded for one linear
     p.total = off;
     return p;
 }
@@ -706,6 +743,7 @@ int check_linear(const dit_linear& L, const char* name) {
     CHECK(L.w != nullptr, DIT_E_NULL, "linear %s: w is NULL", name);
     CHECK(aligned16(L.w), DIT_E_ALIGN, "linear %s: w must be 16-byte aligned", name);
     if (L.s) CHECK(L.wsum && aligned16(L.wsum), DIT_E_NULL, "linear %s: int8 needs a 16-byte aligned wsum", name);
+    CHECK(!(L.s && L.mx_scale), DIT_E_SHAPE, "linear %s: int8 and MXFP4 at once", name);
     return DIT_OK;
 }
 
@@ -734,6 +772,11 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     // linear is W8A8, else the bf16 activation A
     auto lin = [&](const dit_linear& L, const void* A, int64_t N, int64_t K, const EpiParams& ep) -> hipError_t {
         EpiParams e = ep;
+        if (L.mx_scale) {
+            const hipError_t x = launch_mxfp4_expand((const uint8_t*)L.w, L.mx_scale, N, K, ws + p.wx, st);
+            if (x != hipSuccess) return x;
+            return launch_gemm_bf16(A, K, ws + p.wx, T, N, K, e, st);
+        }
         if (!L.s) return launch_gemm_bf16(A, K, L.w, T, N, K, e, st);
         e.a_scale = sa;
         e.a_zero = za;

@@ -1,6 +1,7 @@
-// Pieces of the W8A8 recipe of "Qwen-Image-2.1 W8A8 - FlagOS for Mac"
-// (Quantization and validation): dynamic asymmetric per-token int8 activations
-// and the int8 weight column sums their zero points need.
+// Weight and activation formats of the gated block's linears: the W8A8 recipe
+// of "Qwen-Image-2.1 W8A8 - FlagOS for Mac" (Quantization and validation:
+// dynamic asymmetric per-token int8 activations, and the int8 weight column
+// sums their zero points need) and MXFP4 weights (expanded to bf16 below).
 //
 // Asymmetric codes: the row's range widened to contain 0, lo = min(row, 0),
 // hi = max(row, 0); s = fp32(hi - lo) / 255; zero point z = -128 - rint(lo / s)
@@ -108,7 +109,43 @@ __global__ void __launch_bounds__(256) int8_colsum_kernel(const int8_t* __restri
     if (lane == 0) out[n] = acc;
 }
 
+// MXFP4 ("Qwen_Image-2.1-MXFP4-Paiton", What was quantized): E2M1 codes packed
+// low nibble first, one E8M0 scale per 32 input columns.  One thread per group:
+// 16 code bytes and a scale byte -> 32 bf16 through the hardware fp4 -> bf16
+// conversion with an fp32 scale (an E2M1 value times a power of two is exact in
+// bf16 within its exponent range).
+__global__ void __launch_bounds__(256) mxfp4_expand_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales, int64_t groups,
+                                                           __bf16* __restrict__ out) {
+    const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (g >= groups) return;
+    const v4i c = *reinterpret_cast<const v4i*>(codes + g * 16);
+    const int e = scales[g];
+    const float sc = e == 255 ? __builtin_nanf("") : ldexpf(1.0f, e - 127);
+    v4i o[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // byte b of the word holds elements 2b (low nibble) and 2b + 1
+        const uint32_t word = (uint32_t)c[w];
+        o[w][0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0));
+        o[w][1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1));
+        o[w][2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2));
+        o[w][3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3));
+    }
+    v4i* dst = reinterpret_cast<v4i*>(out + g * 32);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) dst[w] = o[w];
+}
+
 }  // namespace
+
+hipError_t launch_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* out,
+                               hipStream_t st) {
+    const int64_t groups = N * (K / 32);
+    if (groups == 0) return hipSuccess;
+    mxfp4_expand_kernel<<<(unsigned)((groups + 255) / 256), 256, 0, st>>>(codes, scales, groups, (__bf16*)out);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_rows_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                      float* scale, int32_t* zero, hipStream_t st) {

@@ -74,6 +74,8 @@ hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, 
                                 int8_t* q, float* scale, hipStream_t st);
 hipError_t launch_quantize_rows_asym(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx, int8_t* q,
                                      float* scale, int32_t* zero, hipStream_t st);
+hipError_t launch_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* out,
+                               hipStream_t st);
 hipError_t launch_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t st);
 hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
                                      hipStream_t st);

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 2
+#define DIT_ABI_VERSION 3
 
 typedef enum {
     DIT_OK = 0,
@@ -318,6 +318,27 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
                       void* const* v_caches, void* workspace, size_t workspace_bytes,
                       void* stream);
 
+/*
+ * MXFP4 weights ("Qwen_Image-2.1-MXFP4-Paiton", What was quantized and Runtime
+ * precision and quality): E2M1 values packed two per byte, element 2i in the
+ * low nibble of byte i of its row, and one E8M0 scale per group of 32 input
+ * columns: w[n, k] = e2m1(code[n, k]) * 2^(scales[n, k / 32] - 127) (E8M0 255 is
+ * NaN).  The runtime reconstructs the weights and computes in bf16; the
+ * reconstruction is exact in bf16 while the scaled values stay in its normal
+ * range.
+ * dit_mxfp4_expand: codes [N, K/2] uint8, scales [N, K/32] uint8 -> w_bf16 [N, K]
+ * (row stride K).  K % 32 == 0; codes and w_bf16 16-byte aligned.
+ * mxfp4_linear: y = a w^T + bias with w given as MXFP4 (expanded into the
+ * workspace, mxfp4_linear_workspace_bytes(N, K) bytes, then the bf16 linear);
+ * a [M, K] bf16 (row stride lda), y bf16|f32 (row stride ldy).  K % 64 == 0.
+ */
+int dit_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* w_bf16,
+                     void* stream);
+size_t mxfp4_linear_workspace_bytes(int64_t N, int64_t K);
+int mxfp4_linear(const void* a, int64_t M, int64_t K, int64_t lda, const uint8_t* codes, const uint8_t* scales,
+                 const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------ gated-MLP block, per-linear W8A8 */
 
 /*
@@ -326,13 +347,18 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
  * linears run W8A8).  s != NULL: w holds int8 codes [N, K] (symmetric per
  * output channel, scales s [N]) and wsum [N] their row sums (dit_int8_colsum);
  * the activation is quantized asymmetrically per token (dit_quantize_rows_asym).
- * s == NULL: w is bf16 [N, K] and wsum is ignored.  b: fp32 bias [N] or NULL.
+ * mx_scale != NULL: MXFP4 weights (see dit_mxfp4_expand), expanded to bf16 in
+ * the workspace for the call.  Otherwise w is bf16 [N, K] and wsum is ignored.
+ * b: fp32 bias [N] or NULL.
  */
 typedef struct {
     const void* w;
     const float* s;
     const int32_t* wsum;
     const float* b;
+    const uint8_t* mx_scale;   /* != NULL: w holds MXFP4 codes [N, K/2] and these
+                                  E8M0 scales [N, K/32] (dit_mxfp4_expand); s must
+                                  be NULL */
 } dit_linear;
 
 /*

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dq.exported_symbols())
-    assert lib.dit_abi_version() == 2
+    assert lib.dit_abi_version() == 3
 
 
 def test_status_strings():
@@ -265,3 +265,16 @@ def test_gated_validation():
     w.proj = lin
     assert call(cfg, w, wsb=64) == 6                               # workspace too small
     assert lib.dit_gated_block_workspace_bytes(ctypes.byref(cfg), 88, 88) > 0
+
+
+def test_mxfp4_validation():
+    lib = dq.lib()
+    p = 256
+    assert lib.dit_mxfp4_expand(p, p, 4, 48, p, S) == 5                      # K % 32
+    assert lib.dit_mxfp4_expand(p, None, 4, 64, p, S) == 1                   # scales NULL
+    assert lib.dit_mxfp4_expand(264, p, 4, 64, p, S) == 4                    # codes misaligned
+    assert lib.dit_mxfp4_expand(p, p, 0, 64, p, S) == 0                      # N == 0: no-op
+    assert lib.mxfp4_linear_workspace_bytes(16, 64) == 16 * 64 * 2
+    assert lib.mxfp4_linear(p, 8, 64, 64, p, p, None, 16, p, 1, 16, p, 16, S) == 6      # workspace small
+    assert lib.mxfp4_linear(p, 8, 96, 96, p, p, None, 16, p, 1, 16, p, 1 << 20, S) == 5  # K % 64
+    assert lib.mxfp4_linear(p, 8, 64, 64, p, p, None, 16, p, 7, 16, p, 1 << 20, S) == 3  # y dtype
