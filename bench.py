@@ -16,8 +16,9 @@ rows) and the cached step that reuses the prefix K/V (16,384 rows), the latter
 also with the int8/fp8 attention.
 
 Also measured (reported under "gated_recipe_1024px"): one gated-MLP block
-(F 12288) over the same tokens, all-bf16 and with the FlagOS page's W8A8 scope
-(Q/K, proj and gate int8 with asymmetric per-token activations).
+(F 12288) over the same tokens, all-bf16, with the FlagOS page's W8A8 scope
+(Q/K, proj and gate int8 with asymmetric per-token activations), and with all
+six linears stored as MXFP4 (expanded to bf16 per call, bf16 arithmetic).
 
 Also measured (reported under "attn_int8_fp8_1024px"): the same step as the
 timed one with the int8 Q K^T / fp8 P V attention (the pages' later denoising
@@ -353,10 +354,13 @@ def run_gated(args, dq, torch, ditsynth, reps):
     x = torch.empty_like(x0)
     mod = si["mod"][0:1].contiguous()
     res = {"rows": T, "F": F}
-    for label, int8, aq in (("bf16", (), False), ("recipe_w8a8", ("qk", "proj", "gate"), False),
-                            ("recipe_w8a8_attn_int8_fp8", ("qk", "proj", "gate"), True)):
+    shapes = {"qk": (2 * D, D), "v": (D, D), "o": (D, D), "proj": (F, D), "gate": (F, D), "down": (D, F)}
+    mx = {n: ditsynth.mxfp4_weights(*shp, seed=90 + i) for i, (n, shp) in enumerate(shapes.items())}
+    for label, int8, aq, mxw in (("bf16", (), False, None), ("recipe_w8a8", ("qk", "proj", "gate"), False, None),
+                                 ("recipe_w8a8_attn_int8_fp8", ("qk", "proj", "gate"), True, None),
+                                 ("mxfp4_weights", (), False, mx)):
         cfg = dq.block_config("bf16", D, H, F, attn_quant=aq)
-        gw = dq.GatedBlockWeights(arrays, int8)
+        gw = dq.GatedBlockWeights(arrays, int8, mx=mxw)
         ws = torch.empty(dq.gated_workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
 
         def call():
