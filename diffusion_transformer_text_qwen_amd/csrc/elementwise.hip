@@ -66,7 +66,9 @@ __global__ void __launch_bounds__(256) quantize_rows_wave_kernel(const __bf16* _
                                                                  int K, int64_t ldx, int8_t* __restrict__ q,
                                                                  float* __restrict__ scale) {
     const int lane = threadIdx.x % kWave;
-    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    // wave-uniform row (an SGPR): buffer resources built from it then need no
+    // per-lane waterfall loop around each load and store
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     if (row >= M) return;
     const auto xr = raw_rsrc(x + row * ldx, K * 2);
     v4i buf[MAXC];
@@ -241,7 +243,9 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
                                                          __bf16* __restrict__ h, int8_t* __restrict__ qo,
                                                          float* __restrict__ qs) {
     const int lane = threadIdx.x % kWave;
-    const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave;
+    // wave-uniform row (an SGPR): buffer resources built from it then need no
+    // per-lane waterfall loop around each load and store
+    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
     if (row >= M) return;
     const int nchunk = D / 8;
     const auto xr = raw_rsrc(x + row * D, D * 2);
