@@ -27,9 +27,12 @@ constexpr int VT_STRIDE = AK * 2 + 16;  // bytes per d row of the transposed V t
                                         // mod 128, same reason)
 constexpr int KS_BYTES = AK * KS_STRIDE;
 constexpr int VT_BYTES = 128 * VT_STRIDE;
-// Rescale threshold of the online softmax, in log2 units: the running max is
-// only raised when a tile's max exceeds it by more than this, so P <= 2^8.
-constexpr float kRescaleLog2 = 8.0f;
+// Lazy rescale of the online softmax: P of a tile is formed against the
+// running max as it stands, and the max is only raised (the tile's P formed
+// again) when a lane's sum of P over the tile exceeds kRescaleMax, so every P
+// that enters the PV product is at most 2^8.  No per-tile max is computed on
+// the common path.
+constexpr float kRescaleMax = 256.0f;
 
 // Transposed V tile.  Keys are stored in the order the S^T accumulator hands
 // them to a lane for the PV product: within each 16-key block, key k sits at
@@ -165,24 +168,6 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                     if (key >= my_end) scur[kh][j] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kh][j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        // lazy rescale: raise the running max only when this tile exceeds it by
-        // more than 2^kRescaleLog2 (wave-uniform decision)
-        if (__any((mx - m_run) * c_log2 > kRescaleLog2)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
-            m_run = m_new;
-        }
         const float mb = m_run * c_log2;
         // Scores of tile t+1 interleaved with P of tile t: MFMA i (key half
         // i % 2, k-block i / 2) with its operand read four ahead and P of two
@@ -213,6 +198,41 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                 psum = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, psum, false);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // P was formed against the running max.  When a lane's sum over this
+        // tile exceeds kRescaleMax (or is not finite), raise the running max
+        // to the tile's max, rescale, and form P again (a wave-uniform branch,
+        // taken on the first tile and on tiles whose scores climb well above
+        // all earlier ones).
+        if (__any(!(psum <= kRescaleMax))) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kh = 0; kh < 2; ++kh)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kh][j]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const float m_new = fmaxf(m_run, mx);
+            if (m_new > m_run) {
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+                m_run = m_new;
+            }
+            // a row with no visible key so far keeps P = 0
+            const float mb2 = m_run == -INFINITY ? 0.0f : m_run * c_log2;
+            psum = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 32; e += 2) {
+                v2bf p2;
+                p2[0] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16], c_log2, -mb2)));
+                p2[1] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16 + 1], c_log2, -mb2)));
+                pb[e / 8][e % 8] = p2[0];
+                pb[e / 8][e % 8 + 1] = p2[1];
+                psum = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, psum, false);
+            }
         }
         l_run += psum;
         // O^T += V^T P^T (16 keys per MFMA in the S^T lane order; MFMA i: key

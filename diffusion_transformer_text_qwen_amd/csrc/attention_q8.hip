@@ -36,7 +36,11 @@ constexpr int Q8_QB = 128;         // queries per workgroup
 constexpr int Q8_SLOTS = 4;        // LDS ring of (K, V) tile pairs
 constexpr int Q8_SLOT = 2 * TILE_IMG;
 constexpr float kFp8Max = 448.0f;
-constexpr float kRescaleLog2Q8 = 8.0f;   // P <= 2^8 < 448
+// Lazy rescale of the online softmax: P of a tile is formed against the
+// running max as it stands, and the max is only raised (the tile's P formed
+// again) when a lane's sum of P over the tile exceeds kRescaleMaxQ8, so every
+// P that is rounded to e4m3 is at most 2^8 < 448 (no saturation).
+constexpr float kRescaleMaxQ8 = 256.0f;
 
 size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -312,20 +316,6 @@ attn_q8_kernel(const int8_t* __restrict__ Q8, const float* __restrict__ SQ, cons
         }
         // exponent scale of this tile (> 0, so that masked -inf stays -inf)
         const float ct = fmaxf(cq * skh[min(t, nt - 1)], 1e-30f);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, x[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * ct;
-        if (__any(mx - m_run > kRescaleLog2Q8)) {
-            const float m_new = fmaxf(m_run, mx);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
-            m_run = m_new;
-        }
         const float mb = m_run;
         snxt[0] = v16i{};
         snxt[1] = v16i{};
@@ -350,6 +340,40 @@ attn_q8_kernel(const int8_t* __restrict__ Q8, const float* __restrict__ SQ, cons
                 pk[i] = (int)fp8x4(p[0], p[1], p[2], p[3]);
             }
             __builtin_amdgcn_sched_barrier(0);
+        }
+        // P was formed against the running max.  When a lane's sum over this
+        // tile exceeds kRescaleMaxQ8 (or is not finite), raise the running max
+        // to the tile's max, rescale, and form P again (a wave-uniform branch,
+        // taken on the first tile and on tiles whose scores climb well above
+        // all earlier ones).
+        if (__any(!(psum <= kRescaleMaxQ8))) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) mx = fmaxf(mx, x[e]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave)) * ct;
+            const float m_new = fmaxf(m_run, mx);
+            if (m_new > m_run) {
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+                m_run = m_new;
+            }
+            // a row with no visible key so far keeps P = 0
+            const float mb2 = m_run == -INFINITY ? 0.0f : m_run;
+            psum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float p[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    p[e] = __builtin_amdgcn_exp2f(fmaf(x[4 * i + e], ct, -mb2));
+                    psum += p[e];
+                }
+                pk[i] = (int)fp8x4(p[0], p[1], p[2], p[3]);
+            }
         }
         l_run += psum;
         // O^T += V^T P^T: one fp8 MFMA per 32-channel block, loads of tile t+3 in between
