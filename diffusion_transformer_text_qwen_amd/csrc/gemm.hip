@@ -506,6 +506,31 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     for (int i = 0; i < MF; ++i)
 #pragma unroll
         for (int j = 0; j < NF; ++j) acc[i][j] = acc_t{0, 0, 0, 0};
+    if constexpr (I8) {
+        // Zero points of asymmetric activation codes: the wanted integer sum is
+        // sum_k (q - z) w = sum_k q w - z sum_k w, so the accumulators start at
+        // -z[m] * wsum[n] (lane l holds column l % 16 and rows 4 (l / 16) + r of
+        // each 16 x 16 tile).  |z| <= 128 and |wsum| <= 2^23 for K <= 65536: a
+        // 24-bit product, exact in int32.  K-split partial tiles leave the
+        // correction to their reduce.
+        if (ep.a_zero != nullptr && part == nullptr) {
+            int wsj[NF];
+#pragma unroll
+            for (int j = 0; j < NF; ++j) {
+                const int64_t nn = n0 + wn * WTN + j * 16 + lane % 16;
+                wsj[j] = nn < N ? ep.w_sum[nn] : 0;
+            }
+#pragma unroll
+            for (int i = 0; i < MF; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t mm = m0 + wm * WTM + i * 16 + (lane / 16) * 4 + r;
+                    const int z = mm < M ? ep.a_zero[mm] : 0;
+#pragma unroll
+                    for (int j = 0; j < NF; ++j) acc[i][j][r] = -__mul24(z, wsj[j]);
+                }
+        }
+    }
 
     // prologue: stages 0 and 1 in flight, wait for 0, fragments of step 0
     LG_DMA(0);
@@ -616,16 +641,11 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             if (ok) {
                 if constexpr (I8) {
                     const float sa = rows_sa[i][pass];
-                    const int za = ep.a_zero ? ep.a_zero[m] : 0;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        v4i t = *reinterpret_cast<const v4i*>(
+                        // (zero-point correction, if any, is already in the accumulators)
+                        const v4i t = *reinterpret_cast<const v4i*>(
                             reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                        if (ep.a_zero) {
-                            const v4i ws = *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) t[e] -= za * ws[e];
-                        }
                         if constexpr (EV == EV_QKV) {
                             const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
 #pragma unroll
