@@ -137,6 +137,26 @@ def test_attention_q8_matches_oracle(seg_len, T_q, H, scale):
     _check_envelope(got, c, seg_len, T_k)
 
 
+def test_attention_q8_running_max_raised_mid_sequence():
+    """Key norms grow tile by tile and spike late: the running max is raised
+    (and a tile's P formed again) many times after the first tile; every P
+    that is rounded to e4m3 stays below its saturation."""
+    T, H = 704, 2
+    q, k, v = ditsynth.attention_inputs(T, T, H, seed=10)
+    growth = 1.0 + 0.6 * (np.arange(T) // 64)
+    k = k * growth[:, None, None]
+    k[600:606] *= 3.0
+    q, k = ditsynth.to_bf16_grid(q), ditsynth.to_bf16_grid(k)
+    buf = _quantize_on_gpu(q, k, v)
+    c = _decode(buf, T, T, H)
+    for seg_len in ([T], [100, 604]):
+        say("attn q8 rising scores", seg_len)
+        o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+        dq.block_causal_attention_q8(buf, T, T, H, o, seg_len)
+        torch.cuda.synchronize()
+        _check_envelope(host(o), c, seg_len, T)
+
+
 def test_attention_q8_exact_weights():
     """Integer scores (q/k codes with scale 1) and sm_scale = ln 2 make every P a
     power of two that e4m3 holds exactly; with V one-hot (448, scale 1) on a

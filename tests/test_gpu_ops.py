@@ -173,6 +173,28 @@ def test_attention_bf16_special_cases():
         assert np.all(np.abs(got0[i] - ref) <= bf16_ulp(ref) + 2e-3 * np.abs(ref).max())
 
 
+def test_attention_bf16_running_max_raised_mid_sequence():
+    """Key norms grow tile by tile and spike late, so the running max is raised
+    (and a tile's P formed again) many times after the first tile."""
+    T, H = 704, 2
+    q, k, v = ditsynth.attention_inputs(T, T, H, seed=9)
+    growth = 1.0 + 0.6 * (np.arange(T) // 64)
+    k = k * growth[:, None, None]
+    k[600:606] *= 3.0
+    k = ditsynth.to_bf16_grid(k)
+    for seg_len in ([T], [100, 604]):
+        say("attn bf16 rising scores", seg_len)
+        o = torch.empty((T, H, 128), dtype=torch.bfloat16, device=DEV)
+        dq.block_causal_attention(dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16), o,
+                                  seg_len)
+        torch.cuda.synchronize()
+        ref = oracle.attention(q, k, v, seg_len)
+        got = host(o)
+        assert np.all(np.isfinite(got))
+        assert rel_l2(got, ref) < 1e-2
+        assert np.max(np.abs(got - ref)) < 0.05
+
+
 def test_attention_bf16_causal_invariance_and_determinism():
     seg_len = [64, 300, 500]
     T = sum(seg_len)
