@@ -55,15 +55,30 @@ __device__ __forceinline__ float fp8_arg(float v, float s) {
     if (s == 0.0f) return 0.0f;
     return fminf(fmaxf(__fdiv_rn(v, s), -kFp8Max), kFp8Max);
 }
+// The same argument through the reciprocal product t = v * inv (inv =
+// fl(1 / s)): t lies within 3 ulps of fl(v / s), so both round to the same
+// e4m3 value unless t is within a few ulps of an e4m3 rounding midpoint
+// (normal range: the 20 fp32 mantissa bits below e4m3's 3 at 0x80000;
+// subnormal range |t| < 2^-6: an odd multiple of 2^-10); those take the division.
+__device__ __forceinline__ float fp8_arg_fast(float v, float s, float inv) {
+    if (s == 0.0f) return 0.0f;
+    const float t = v * inv;
+    const float at = fabsf(t);
+    bool near;
+    if (at >= 0x1p-6f) {
+        const int low = (int)(__builtin_bit_cast(uint32_t, at) & 0xFFFFFu);
+        near = abs(low - 0x80000) <= 8;
+    } else {
+        const float u = at * 512.0f;
+        near = fabsf(u - floorf(u) - 0.5f) < 0x1p-12f;
+    }
+    if (near) return fp8_arg(v, s);
+    return fminf(fmaxf(t, -kFp8Max), kFp8Max);
+}
 __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
     int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
     w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
     return (uint32_t)w;
-}
-
-__device__ __forceinline__ uint32_t pack_i8x4(int8_t a, int8_t b, int8_t c, int8_t d) {
-    return (uint32_t)(uint8_t)a | ((uint32_t)(uint8_t)b << 8) | ((uint32_t)(uint8_t)c << 16) |
-           ((uint32_t)(uint8_t)d << 24);
 }
 
 __global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, int n) {
@@ -71,10 +86,16 @@ __global__ void __launch_bounds__(256) fill_u32_kernel(uint32_t* p, int n) {
     if (i < n) p[i] = 0u;
 }
 
-// q: 16 lanes per (token, head) row, 8 values each.
+// q: 16 lanes per (token, head) row, 8 values each.  The first nfill threads
+// also clear the V channel amax words that the K kernel raises next.
 __global__ void __launch_bounds__(256) attn_quant_q_kernel(const __bf16* __restrict__ q, int64_t ldq, int T_q,
                                                            int H, int8_t* __restrict__ q8,
-                                                           float* __restrict__ sq) {
+                                                           float* __restrict__ sq, uint32_t* __restrict__ vamax,
+                                                           int nfill) {
+    {
+        const int gi = blockIdx.x * 256 + threadIdx.x;
+        if (gi < nfill) vamax[gi] = 0u;
+    }
     const int64_t g = (int64_t)blockIdx.x * 16 + threadIdx.x / 16;
     const int sub = threadIdx.x % 16;
     const bool ok = g < (int64_t)T_q * H;
@@ -92,10 +113,10 @@ __global__ void __launch_bounds__(256) attn_quant_q_kernel(const __bf16* __restr
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) a = fmaxf(a, __shfl_xor(a, m, kWave));
     const float s = __fdiv_rn(a, 127.0f);
+    // codes of v / s (IEEE division, ties to even) through the reciprocal
+    // product with a near-tie fallback, as for the per-token activations
+    const uint2 o = quant8(v, s, __fdiv_rn(1.0f, s), s >= 0x1p-100f);
     if (!ok) return;
-    uint2 o;
-    o.x = pack_i8x4(quant_code(v[0], s), quant_code(v[1], s), quant_code(v[2], s), quant_code(v[3], s));
-    o.y = pack_i8x4(quant_code(v[4], s), quant_code(v[5], s), quant_code(v[6], s), quant_code(v[7], s));
     *reinterpret_cast<uint2*>(q8 + ((int64_t)h * T_q + t) * 128 + sub * 8) = o;
     if (sub == 0) sq[(int64_t)h * T_q + t] = s;
 }
@@ -130,16 +151,20 @@ __global__ void __launch_bounds__(256) attn_quant_k_kernel(const __bf16* __restr
     __syncthreads();
     a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float s = __fdiv_rn(a, 127.0f);
+    const float inv = __fdiv_rn(1.0f, s);
+    const bool fast = s >= 0x1p-100f;
     int8_t* img = k8 + ((int64_t)h * nt + t) * TILE_IMG;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         const int c = part * 2 + half;
-        v4i o;
+        float lo[8], hi[8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const float* x = kv + half * 16 + w * 4;
-            o[w] = (int)pack_i8x4(quant_code(x[0], s), quant_code(x[1], s), quant_code(x[2], s), quant_code(x[3], s));
+        for (int e = 0; e < 8; ++e) {
+            lo[e] = kv[half * 16 + e];
+            hi[e] = kv[half * 16 + 8 + e];
         }
+        const uint2 a8 = quant8(lo, s, inv, fast), b8 = quant8(hi, s, inv, fast);
+        const v4i o = {(int)a8.x, (int)a8.y, (int)b8.x, (int)b8.y};
         *reinterpret_cast<v4i*>(img + r * 128 + ((c ^ (r & 7)) << 4)) = o;
     }
     if (tid == 0) sk[(int64_t)h * nt + t] = s;
@@ -191,9 +216,10 @@ __global__ void __launch_bounds__(256) attn_quant_v_kernel(const __bf16* __restr
     __syncthreads();
     const int ch = tid / 2, ph = tid % 2;
     const float s = __fdiv_rn(__builtin_bit_cast(float, vamax[h * 128 + ch]), kFp8Max);
+    const float inv = __fdiv_rn(1.0f, s);
     float r[32];
 #pragma unroll
-    for (int b = 0; b < 32; ++b) r[b] = fp8_arg((float)tile[vkey_of_pos(ph * 32 + b)][ch], s);
+    for (int b = 0; b < 32; ++b) r[b] = fp8_arg_fast((float)tile[vkey_of_pos(ph * 32 + b)][ch], s, inv);
     uint8_t* row = v8 + ((int64_t)h * nt + t) * TILE_IMG + ch * 64;
     const int sw = (ch >> 1) & 3;
 #pragma unroll
@@ -467,10 +493,14 @@ hipError_t launch_attn_quantize(const void* q, const void* k, const void* v, int
     const AttnQ8Layout L = attn_q8_layout(T_q, T_k, H);
     uint8_t* b = (uint8_t*)buf;
     uint32_t* vamax = (uint32_t*)(b + L.vamax);
-    fill_u32_kernel<<<(unsigned)((H * 128 + 255) / 256), 256, 0, st>>>(vamax, H * 128);
+    // the Q launch clears the V amax words when it has a thread for each
+    const int64_t q_threads = (T_q * H + 15) / 16 * 256;
+    const bool fold = T_q > 0 && q_threads >= (int64_t)H * 128;
+    if (!fold) fill_u32_kernel<<<(unsigned)((H * 128 + 255) / 256), 256, 0, st>>>(vamax, H * 128);
     if (T_q > 0)
         attn_quant_q_kernel<<<(unsigned)((T_q * H + 15) / 16), 256, 0, st>>>(
-            (const __bf16*)q, ldq, (int)T_q, H, (int8_t*)(b + L.q8), (float*)(b + L.sq));
+            (const __bf16*)q, ldq, (int)T_q, H, (int8_t*)(b + L.q8), (float*)(b + L.sq), vamax,
+            fold ? H * 128 : 0);
     if (L.nt > 0) {
         const dim3 grid((unsigned)L.nt, (unsigned)H);
         attn_quant_k_kernel<<<grid, 256, 0, st>>>((const __bf16*)k, ldk, (const __bf16*)v, ldv, (int)T_k,
