@@ -118,6 +118,8 @@ ATTN_CASES = [
     ([64, 256, 700], 1020, 1, 1.0),
     ([300], 300, 2, 3.0),                # peaked scores: exercises the running-max rescale
     ([200], 200, 1, 0.05),               # nearly uniform attention
+    ([100, 37], 1, 2, 1.0),              # a single query (the last row) against a cached prefix
+    ([5, 17, 1, 64, 3, 40, 9, 70, 2, 33, 11, 8, 60, 1, 25, 30], 379, 1, 1.0),   # 16 segments
 ]
 
 

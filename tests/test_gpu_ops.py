@@ -137,6 +137,8 @@ ATTN_CASES = [
     ([40, 90, 333], 333, 3),          # cached step: queries are the last segment
     ([256, 1024, 700], 1980, 1),
     ([300], 300, 2),                  # one segment: plain full attention
+    ([100, 37], 1, 2),                # a single query (the last row) against a cached prefix
+    ([5, 17, 1, 64, 3, 40, 9, 70, 2, 33, 11, 8, 60, 1, 25, 30], 379, 1),   # the maximum of 16 segments
 ]
 
 
