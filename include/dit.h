@@ -162,9 +162,10 @@ int block_causal_attention(const void* q, const void* k, const void* v, void* o,
  *   v: e4m3 per (head, channel) over all T_k keys, scale amax/448;
  *   codes by an IEEE fp32 division, round half to even (v saturates at 448);
  *   scores = exact int32 dot products times sm_scale and the q and k scales;
- *   P = exp of the score minus a running row maximum (at most 2^8 below the
- *   final one), rounded to e4m3 for the P V product; the softmax normalizer
- *   sums the unrounded P; o is bf16.
+ *   P = exp of the score minus a running row maximum, raised lazily so that
+ *   every P is at most 2^8 when formed (earlier sums are rescaled when it
+ *   rises), rounded to e4m3 for the P V product; the softmax normalizer sums
+ *   the unrounded P; o is bf16.
  *
  * dit_attn_q8_bytes: size of the operand buffer for (T_q, T_k, H); if
  * offsets != NULL writes the byte offsets of its 7 parts (256-aligned):
