@@ -20,6 +20,10 @@ Also measured (reported under "gated_recipe_1024px"): one gated-MLP block
 (Q/K, proj and gate int8 with asymmetric per-token activations), and with all
 six linears stored as MXFP4 (expanded to bf16 per call, bf16 arithmetic).
 
+Also measured (reported under "small_blocks"): one block of the 256x256
+generation in bf16 ([64 text | 256 image] tokens) and one of the 512x512
+generation in W8A8 ([128 text | 1024 image] tokens).
+
 Also measured (reported under "attn_int8_fp8_1024px"): the same step as the
 timed one with the int8 Q K^T / fp8 P V attention (the pages' later denoising
 steps), and the 40-step loop with the first 7 steps bf16 attention, the rest
@@ -336,6 +340,65 @@ def run_edit(args, dq, torch, ditsynth, reps):
     return res
 
 
+def run_small(args, dq, torch, ditsynth, reps):
+    """One block each of the 256^2 (bf16) and 512^2 (W8A8) generations."""
+    dev = "cuda"
+    res = {}
+    for idx in (1, 2):
+        w = ditsynth.workload(idx)
+        D, H, F, T, L = w.D, w.H, w.F, w.T, w.text
+        t = {}
+        for name, a in ditsynth.device_block_weights(w, 0, dev):
+            if name.startswith("w_") and w.mode == "w8a8":
+                q = torch.empty(a.shape, dtype=torch.int8, device=dev)
+                s = torch.empty(a.shape[0], dtype=torch.float32, device=dev)
+                dq.quantize_rows(a, q, s)
+                t[name], t["s" + name[1:]] = q, s
+            elif name.startswith("w_"):
+                t[name] = a.to(torch.bfloat16).contiguous()
+            else:
+                t[name] = a
+        bw = dq.BlockWeights.from_device(t, w.mode)
+        cfg = dq.block_config(w.mode, D, H, F)
+        g = torch.Generator(device=dev)
+        g.manual_seed(idx)
+        x0 = torch.randn((T, D), generator=g, device=dev).to(torch.bfloat16)
+        mod = (torch.randn((1, 6, D), generator=g, device=dev) * 0.1).contiguous()
+        cos = torch.empty((T, 64), dtype=torch.float32, device=dev)
+        sin = torch.empty((T, 64), dtype=torch.float32, device=dev)
+        dq.rope_tables(L, w.images, 0, T, cos, sin)
+        kc = torch.empty((T, H, 128), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        ws = torch.empty(dq.workspace_bytes(cfg, T, T), dtype=torch.uint8, device=dev)
+        x = torch.empty_like(x0)
+
+        def call():
+            x.copy_(x0)
+            dq.block_forward(cfg, bw, x, mod, [0] * len(w.seg_len), cos, sin, w.seg_len, kc, vc, ws)
+
+        call()
+        torch.cuda.synchronize()
+        dq.profile_begin(reps * 10 + 4)
+        for _ in range(reps):
+            call()
+        torch.cuda.synchronize()
+        prof = dq.profile_end()
+        blk_ms = sum(p["ms"] for p in prof.values()) / reps
+        att = prof["attention"]
+        att_tf = 4 * D * attn_pairs(w.seg_len, T) / (att["ms"] / att["count"] * 1e-3) / 1e12
+        gops = sum(gemm_ops(T, D, F).values())
+        g_rate = gops / (sum(prof[s]["ms"] for s in GEMM_SITES) / reps * 1e-3) / 1e12
+        peak = PEAK_INT8_TOPS if w.mode == "w8a8" else PEAK_BF16_TFLOPS
+        res[w.name] = {"rows": T, "mode": w.mode, "block_ms": round(blk_ms, 3),
+                       "block_tokens_per_s": round(T / (blk_ms * 1e-3), 1),
+                       "gemm_rate": round(g_rate, 1), "gemm_unit": "TOPS" if w.mode == "w8a8" else "TFLOPS",
+                       "gemm_frac_peak": round(g_rate / peak, 4),
+                       "attention_tflops": round(att_tf, 1),
+                       "finite": bool(torch.isfinite(x.float()).all().item())}
+        del bw, t, ws, kc, vc
+    return res
+
+
 def run_gated(args, dq, torch, ditsynth, reps):
     """One gated-MLP block (F = 12288) over the 1024^2 token layout: all linears
     bf16, and the FlagOS page's W8A8 scope (Q/K, proj, gate int8 with asymmetric
@@ -481,6 +544,7 @@ def main():
     if not args.no_edit:
         line["edit_2048px"] = run_edit(args, dq, torch, ditsynth, args.edit_reps)
         line["gated_recipe_1024px"] = run_gated(args, dq, torch, ditsynth, args.edit_reps)
+        line["small_blocks"] = run_small(args, dq, torch, ditsynth, args.edit_reps)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on one block ...")
         line["cpu_baseline"] = cpu_baseline(ditsynth)

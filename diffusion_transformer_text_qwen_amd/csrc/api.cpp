@@ -503,7 +503,8 @@ Plan plan(const dit_block_config* cfg, int64_t T, int64_t T_k) {
     p.g = take(T * F * act);
     p.g8 = take(q8 ? T * F : 0);
     p.sg = take(q8 ? T * 4 : 0);
-    p.split = take(q8 ? (size_t)kSplitPartialBytes : 0);
+    // K-split partial sums of the MFMA GEMMs (int32 for W8A8, fp32 for bf16)
+    p.split = take(cfg->mode != DIT_MODE_F32 ? (size_t)kSplitPartialBytes : 0);
     p.aq = take(cfg->attn_quant ? attn_q8_layout(T, T_k, cfg->H).total : 0);
     p.total = off;
     return p;
@@ -595,7 +596,12 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
             e.split_bytes = kSplitPartialBytes;
             return launch_gemm_i8(A8, (const int8_t*)Wt, T, N, K, e, st);
         }
-        if (bf) return launch_gemm_bf16(A, K, Wt, T, N, K, ep, st);
+        if (bf) {
+            EpiParams e = ep;
+            e.split_partial = split_partial;
+            e.split_bytes = kSplitPartialBytes;
+            return launch_gemm_bf16(A, K, Wt, T, N, K, e, st);
+        }
         return launch_gemm_f32((const float*)A, K, (const float*)Wt, T, N, K, ep, st);
     };
 
@@ -772,6 +778,8 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     // linear is W8A8, else the bf16 activation A
     auto lin = [&](const dit_linear& L, const void* A, int64_t N, int64_t K, const EpiParams& ep) -> hipError_t {
         EpiParams e = ep;
+        e.split_partial = split_partial;
+        e.split_bytes = kSplitPartialBytes;
         if (L.mx_scale) {
             const hipError_t x = launch_mxfp4_expand((const uint8_t*)L.w, L.mx_scale, N, K, ws + p.wx, st);
             if (x != hipSuccess) return x;
@@ -782,8 +790,6 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
         e.a_zero = za;
         e.w_scale = L.s;
         e.w_sum = L.wsum;
-        e.split_partial = split_partial;
-        e.split_bytes = kSplitPartialBytes;
         return launch_gemm_i8(a8, (const int8_t*)L.w, T, N, K, e, st);
     };
     auto quant = [&](const void* A, int64_t K) -> hipError_t {

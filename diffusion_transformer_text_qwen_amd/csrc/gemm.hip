@@ -361,10 +361,11 @@ constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
 
 // Partial last round: with T tiles on C compute units, the C workgroups of one
 // persistent launch each take floor(T/C) whole tiles; each of the r remaining
-// tiles is split into S K ranges, one per workgroup, which stores its int32
-// partial sums.  A second launch adds the partials (integer addition: exact in
-// any order) and applies the epilogue; the kernel boundary orders the partial
-// stores before their reads.  The K range runs before the whole tiles, so its
+// tiles (all T when T < C) is split into S K ranges, one per workgroup, which
+// stores its partial sums (int32 for int8 operands, fp32 for bf16).  A second
+// launch adds the partials (int32: exact in any order; fp32: in K order) and
+// applies the epilogue; the kernel boundary orders the partial stores before
+// their reads.  The K range runs before the whole tiles, so its
 // partial stores overlap them.  For long K loops (more than 64 steps) two
 // launches measured faster: whole tiles, then the K ranges (the same kernel
 // with full = 0).
@@ -621,16 +622,14 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
         for (int pass = 0; pass < 16 / RPP; ++pass) {
             const int er = pass * RPP + er0;
             const int64_t m = m0 + wm * WTM + i * 16 + er;
-            if constexpr (I8) {
-                if (part != nullptr) {
-                    // partial sums of this K range, row-major 256 x 256
-                    int32_t* pp = part + (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
+            if (part != nullptr) {
+                // partial sums of this K range (int32, or fp32 bits), row-major 256 x 256
+                int32_t* pp = part + (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<v4i*>(pp + 4 * q) = *reinterpret_cast<const v4i*>(
-                            reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                    continue;
-                }
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<v4i*>(pp + 4 * q) = *reinterpret_cast<const v4i*>(
+                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                continue;
             }
             float v[16];
             int32_t ai[16];
@@ -710,7 +709,7 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     // multiple of G, XCD x takes the contiguous tile range [x full/8,
     // (x+1) full/8) so that tiles sharing rows of A or W share an L2.  One call
     // site keeps one copy of the tile code.
-    const bool chunk = I8 && lp.S > 0 && b < lp.r * lp.S;
+    const bool chunk = lp.S > 0 && b < lp.r * lp.S;
     const bool xcd = G % 8 == 0 && lp.full % G == 0;
     const int jobs = (lp.full + G - 1) / G;
     const int cj = chunk ? 0 : -1;   // job index of the K range
@@ -741,9 +740,18 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 constexpr int kNumCU = 256;
 constexpr size_t L_LDS = (size_t)L_SLOTS * L_STAGE_BYTES;
 
-static bool use_large(int64_t M, int64_t N) {
+// The 256 x 256 persistent kernel takes a shape when its tiles, or their K-split
+// ranges, occupy at least three quarters of the compute units; smaller shapes
+// go to the 128 x 128 kernel.
+static bool use_large(int64_t M, int64_t N, int nk, bool can_split) {
     const int64_t tiles = ((M + L_BM - 1) / L_BM) * ((N + L_BN - 1) / L_BN);
-    return tiles >= kNumCU;
+    if (tiles >= kNumCU) return true;
+    int64_t jobs = tiles;
+    if (can_split) {
+        const int64_t S = std::min<int64_t>(std::min<int64_t>(kNumCU / tiles, 16), nk / 8);
+        if (S >= 2) jobs = tiles * S;
+    }
+    return 4 * jobs >= 3 * kNumCU;
 }
 
 static unsigned large_grid(int64_t M, int64_t N) {
@@ -775,13 +783,14 @@ static int num_cus() {
 }
 
 // Split plan for T tiles of nk K steps: split only the r tiles of the last,
-// partial round into S <= C / r ranges of at least 8 steps each.
+// partial round (every tile when T < C) into S <= C / r ranges of at least 8
+// steps each.
 static int plan_split(int64_t tiles, int nk, const EpiParams& ep, int64_t* full) {
     *full = tiles;
     if (!ep.split_partial) return 0;
     const int C = num_cus();
     const int64_t R = tiles / C, r = tiles - R * C;
-    if (R == 0 || r == 0) return 0;
+    if (r == 0) return 0;
     int S = (int)std::min<int64_t>(C / r, 16);
     S = std::min(S, nk / 8);
     if (S < 2 || r * S * (int64_t)L_BM * L_BN * 4 > ep.split_bytes) return 0;
@@ -789,9 +798,11 @@ static int plan_split(int64_t tiles, int nk, const EpiParams& ep, int64_t* full)
     return S;
 }
 
-// Sum of the S partial tiles of each split tile, then the int8 epilogue.  One
+// Sum of the S partial tiles of each split tile, then the epilogue.  One
 // workgroup per 16 rows of a tile; thread t owns 16 consecutive columns.
-template <int EV>
+// int8: int32 partials (exact in any order), then the zero-point correction
+// and the scales; bf16: fp32 partials added in K order.
+template <bool I8, int EV>
 __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N, EpiParams ep, int32_t tau0,
                                                            int32_t S) {
     const int tiles_m = (int)((M + L_BM - 1) / L_BM);
@@ -802,13 +813,16 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     const int row = rb * 16 + threadIdx.x / 16, col = (threadIdx.x % 16) * 16;
     const int64_t m = tm0 + row, n = tn0 + col;
     if (m >= M || n >= N) return;
-    v4i sum[4] = {};
     const int32_t* part = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + row * L_BN + col;
+    QkvAux aux;
     if constexpr (EV == EV_QKV) {
-        // 16 threads per row; a head's 128 columns are 8 neighbouring lanes
-        QkvAux aux;
         qkv_gain16(ep, n, aux);
         qkv_rope16(ep, m, n, aux);
+    }
+    float v[16];
+    int32_t ai[16] = {};
+    if constexpr (I8) {
+        v4i sum[4] = {};
         for (int s2 = 0; s2 < S; ++s2)
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -819,41 +833,36 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
             for (int q = 0; q < 4; ++q) sum[q] -= za * *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
         }
         const float sa = ep.a_scale[m];
-        float v[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * q + e] = (float)sum[q][e] * sa * sw[e];
+            for (int e = 0; e < 4; ++e) {
+                ai[4 * q + e] = sum[q][e];
+                v[4 * q + e] = (float)sum[q][e] * sa * sw[e];
+            }
         }
+    } else {
+        v4f sum[4] = {};
+        for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                sum[q] += *reinterpret_cast<const v4f*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = sum[q][e];
+    }
+    if constexpr (EV == EV_QKV) {
+        // 16 threads per row; a head's 128 columns are 8 neighbouring lanes
         float ss = qkv_prep16(ep, n, v);
         ss += __shfl_xor(ss, 1, kWave);
         ss += __shfl_xor(ss, 2, kWave);
         ss += __shfl_xor(ss, 4, kWave);
         qkv_finish16(ep, m, n, v, ss, aux);
-        return;
+    } else {
+        epilogue16<EV>(ep, m, n, v, ai);
     }
-    for (int s2 = 0; s2 < S; ++s2)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
-    if (ep.a_zero) {
-        const int za = ep.a_zero[m];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sum[q] -= za * *reinterpret_cast<const v4i*>(ep.w_sum + n + 4 * q);
-    }
-    const float sa = ep.a_scale[m];
-    float v[16];
-    int32_t ai[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            ai[4 * q + e] = sum[q][e];
-            v[4 * q + e] = (float)sum[q][e] * sa * sw[e];
-        }
-    }
-    epilogue16<EV>(ep, m, n, v, ai);
 }
 
 template <bool I8, int EV>
@@ -861,7 +870,8 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
                         const EpiParams& ep, hipStream_t st) {
     constexpr int kWN = EV == EV_QKV ? 2 : 4;
     // the large kernel addresses each operand with 32-bit buffer offsets
-    if (use_large(M, N) && lda_b % 16 == 0 && Kb % L_SK == 0 && M * lda_b < ((int64_t)1 << 31) &&
+    if (use_large(M, N, (int)(Kb / L_BK), ep.split_partial != nullptr) && lda_b % 16 == 0 &&
+        Kb % L_SK == 0 && M * lda_b < ((int64_t)1 << 31) &&
         N * Kb < ((int64_t)1 << 31)) {
         static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
@@ -871,21 +881,25 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
         }
         const int64_t tiles = large_grid(M, N);
         int64_t full = tiles;
-        const int S = I8 ? plan_split(tiles, (int)(Kb / L_BK), ep, &full) : 0;
+        const int S = plan_split(tiles, (int)(Kb / L_BK), ep, &full);
         const int32_t r = S ? (int32_t)(tiles - full) : 0;
         const int C = num_cus();
         if (S && Kb / L_BK > 64) {
             // long K loops: whole tiles, then the K ranges of the split tiles
-            gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
-                a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
+            if (full > 0)
+                gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
+                    a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
             gemm_large_kernel<I8, EV, kWN><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
                 a, lda_b, w, M, N, Kb, ep, LargePlan{0, (int32_t)full, r, S});
         } else {
-            // persistent: one workgroup per compute unit (use_large guarantees tiles >= C)
-            gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, tiles), L_THREADS, L_LDS, st>>>(
-                a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, r, S});
+            // persistent: at most one workgroup per compute unit, and one for
+            // each split range (r * S <= C)
+            const int64_t G = std::min<int64_t>(C, std::max<int64_t>(full > 0 ? tiles : 0, (int64_t)r * S));
+            gemm_large_kernel<I8, EV, kWN><<<(unsigned)(G > 0 ? G : std::min<int64_t>(C, tiles)), L_THREADS,
+                                             L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
+                                                          LargePlan{(int32_t)full, (int32_t)full, r, S});
         }
-        if (S) split_reduce_kernel<EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
+        if (S) split_reduce_kernel<I8, EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
     }
     else if constexpr (EV == EV_QKV) {
         // store the QKV output, then the separate norm/RoPE kernel

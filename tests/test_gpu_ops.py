@@ -46,10 +46,14 @@ def test_quantize_outlier_weights_bit_exact():
 
 @pytest.mark.parametrize("M,N,K,ws", [(1, 16, 128, False), (77, 272, 384, False), (300, 512, 4096, True),
                                       (129, 128, 16384, False), (4429, 4144, 256, False), (4096, 4096, 640, False),
-                                      (4352, 4096, 1024, True), (4429, 4144, 2048, True)])
+                                      (4352, 4096, 1024, True), (4429, 4144, 2048, True),
+                                      (1024, 15360, 256, False), (1152, 3072, 4096, True),
+                                      (1152, 1536, 8192, True)])
 def test_w8a8_linear_exact_accumulators(M, N, K, ws):
-    """ws=True passes a workspace: tiles of a partial last round are split along K
-    (272 / 306 tiles on 256 CUs here), partial int32 sums reduced by the last arriver."""
+    """ws=True passes a workspace: tiles of a partial last round (272 / 306 tiles on
+    256 CUs), or every tile of a launch with fewer tiles than CUs (60 and 30 tiles,
+    the second with a long K loop), are split along K and their partial int32 sums
+    added by a reduce launch; 240 tiles without a workspace run as one partial round."""
     say("w8a8", M, N, K, ws)
     a, b, sa, sb, bias = ditsynth.int8_operands(M, N, K, seed=M * 7 + N)
     acc = torch.empty((M, N), dtype=torch.int32, device=DEV)
