@@ -643,10 +643,11 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     if (cfg->attn_quant) {
         {
             ProfScope ps(DIT_SITE_ATTN_QUANT, st);
-            RUN(launch_attn_quantize(qb, k_cache, v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st), "attn_quantize");
+            RUN(launch_attn_quantize(qb, k_cache, v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st, false),
+                "attn_quantize");
         }
         ProfScope ps(DIT_SITE_ATTENTION, st);
-        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st), "attention_q8");
+        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st, qb, D), "attention_q8");
     } else {
     ProfScope ps(DIT_SITE_ATTENTION, st);
     if (bf)
@@ -827,11 +828,11 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     if (cfg->attn_quant) {
         {
             ProfScope ps(DIT_SITE_ATTN_QUANT, st);
-            RUN(launch_attn_quantize(qb, io->k_cache, io->v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st),
+            RUN(launch_attn_quantize(qb, io->k_cache, io->v_cache, T, io->T_k, H, D, D, D, ws + p.aq, st, false),
                 "attn_quantize");
         }
         ProfScope ps(DIT_SITE_ATTENTION, st);
-        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st), "attention_q8");
+        RUN(launch_attention_q8(ws + p.aq, T, io->T_k, H, ob, D, segs, scale, st, qb, D), "attention_q8");
     } else {
         ProfScope ps(DIT_SITE_ATTENTION, st);
         RUN(launch_attention_bf16(qb, io->k_cache, io->v_cache, ob, T, io->T_k, H, D, D, D, D, segs, scale, st),

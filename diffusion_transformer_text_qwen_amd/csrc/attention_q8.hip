@@ -241,10 +241,12 @@ __global__ void __launch_bounds__(256) attn_quant_v_kernel(const __bf16* __restr
 // 4-slot LDS ring, tile t+3 loaded while tile t is processed; one barrier per
 // tile.  Lane l owns query l % 32 of its wave; its 32 scores of a tile are the
 // keys of the two 32-key halves handed out by the 32x32 accumulator layout.
+template <bool QBF16>
 __global__ void __launch_bounds__(256, 2)
 attn_q8_kernel(const int8_t* __restrict__ Q8, const float* __restrict__ SQ, const uint8_t* __restrict__ K8,
                const float* __restrict__ SK, const uint8_t* __restrict__ V8, const float* __restrict__ SV,
-               __bf16* __restrict__ O, int T_q, int T_k, int nt, int ldo, AttnSegs sg, float c_log2) {
+               __bf16* __restrict__ O, int T_q, int T_k, int nt, int ldo, AttnSegs sg, float c_log2,
+               const __bf16* __restrict__ QB, int64_t ldqb) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[Q8_SLOTS * Q8_SLOT];
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     typedef int v8i __attribute__((ext_vector_type(8)));
@@ -265,12 +267,50 @@ attn_q8_kernel(const int8_t* __restrict__ Q8, const float* __restrict__ SQ, cons
 
     // Q^T fragments (B operand): dims kb*32 + hh*16 .. +16 of this lane's query
     v4i qf[4];
-    {
+    float cq;
+    if constexpr (QBF16) {
+        // the query row's int8 codes formed here from bf16 Q, exactly as
+        // attn_quant_q_kernel forms them: amax over the row's 128 dims (this
+        // lane's 64 and lane l^32's), s = amax / 127, codes of v / s
+        float v[4][16];
+        float a = 0.0f;
+        {
+            const __bf16* qrow = QB + (int64_t)(q_ok ? qi : 0) * ldqb + h * 128 + hh * 16;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const v8bf x0 = q_ok ? *reinterpret_cast<const v8bf*>(qrow + kb * 32) : v8bf{};
+                const v8bf x1 = q_ok ? *reinterpret_cast<const v8bf*>(qrow + kb * 32 + 8) : v8bf{};
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    v[kb][e] = (float)x0[e];
+                    v[kb][8 + e] = (float)x1[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(v[kb][e]));
+            }
+        }
+        a = fmaxf(a, __shfl_xor(a, 32, kWave));
+        const float s = __fdiv_rn(a, 127.0f);
+        const float inv = __fdiv_rn(1.0f, s);
+        const bool fast = s >= 0x1p-100f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            float lo[8], hi[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lo[e] = v[kb][e];
+                hi[e] = v[kb][8 + e];
+            }
+            const uint2 c0 = quant8(lo, s, inv, fast), c1 = quant8(hi, s, inv, fast);
+            qf[kb] = v4i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y};
+        }
+        cq = q_ok ? s * c_log2 : 0.0f;
+    } else {
         const int8_t* qrow = Q8 + ((int64_t)h * T_q + (q_ok ? qi : 0)) * 128 + hh * 16;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) qf[kb] = q_ok ? *reinterpret_cast<const v4i*>(qrow + kb * 32) : v4i{};
+        cq = q_ok ? SQ[(int64_t)h * T_q + qi] * c_log2 : 0.0f;
     }
-    const float cq = q_ok ? SQ[(int64_t)h * T_q + qi] * c_log2 : 0.0f;
     const float* skh = SK + (int64_t)h * nt;
 
     // tile images of this head; every load is inside [0, nt * 8 KB)
@@ -489,11 +529,12 @@ AttnQ8Layout attn_q8_layout(int64_t T_q, int64_t T_k, int H) {
 }
 
 hipError_t launch_attn_quantize(const void* q, const void* k, const void* v, int64_t T_q, int64_t T_k, int H,
-                                int64_t ldq, int64_t ldk, int64_t ldv, void* buf, hipStream_t st) {
+                                int64_t ldq, int64_t ldk, int64_t ldv, void* buf, hipStream_t st, bool with_q) {
     const AttnQ8Layout L = attn_q8_layout(T_q, T_k, H);
     uint8_t* b = (uint8_t*)buf;
     uint32_t* vamax = (uint32_t*)(b + L.vamax);
     // the Q launch clears the V amax words when it has a thread for each
+    if (!with_q) T_q = 0;
     const int64_t q_threads = (T_q * H + 15) / 16 * 256;
     const bool fold = T_q > 0 && q_threads >= (int64_t)H * 128;
     if (!fold) fill_u32_kernel<<<(unsigned)((H * 128 + 255) / 256), 256, 0, st>>>(vamax, H * 128);
@@ -512,16 +553,24 @@ hipError_t launch_attn_quantize(const void* q, const void* k, const void* v, int
 }
 
 hipError_t launch_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int H, void* o, int64_t ldo,
-                               const AttnSegs& segs, float sm_scale, hipStream_t st) {
+                               const AttnSegs& segs, float sm_scale, hipStream_t st, const void* q_bf16,
+                               int64_t ldq) {
     if (T_q == 0) return hipSuccess;
     const AttnQ8Layout L = attn_q8_layout(T_q, T_k, H);
     const uint8_t* b = (const uint8_t*)buf;
     const float c = sm_scale * 1.4426950408889634f;
     const dim3 grid((unsigned)((T_q + Q8_QB - 1) / Q8_QB), (unsigned)H);
-    attn_q8_kernel<<<grid, 256, 0, st>>>((const int8_t*)(b + L.q8), (const float*)(b + L.sq),
-                                         (const uint8_t*)(b + L.k8), (const float*)(b + L.sk),
-                                         (const uint8_t*)(b + L.v8), (const float*)(b + L.sv), (__bf16*)o,
-                                         (int)T_q, (int)T_k, (int)L.nt, (int)ldo, segs, c);
+    if (q_bf16)
+        attn_q8_kernel<true><<<grid, 256, 0, st>>>(nullptr, nullptr, (const uint8_t*)(b + L.k8),
+                                                   (const float*)(b + L.sk), (const uint8_t*)(b + L.v8),
+                                                   (const float*)(b + L.sv), (__bf16*)o, (int)T_q, (int)T_k,
+                                                   (int)L.nt, (int)ldo, segs, c, (const __bf16*)q_bf16, ldq);
+    else
+        attn_q8_kernel<false><<<grid, 256, 0, st>>>((const int8_t*)(b + L.q8), (const float*)(b + L.sq),
+                                                    (const uint8_t*)(b + L.k8), (const float*)(b + L.sk),
+                                                    (const uint8_t*)(b + L.v8), (const float*)(b + L.sv),
+                                                    (__bf16*)o, (int)T_q, (int)T_k, (int)L.nt, (int)ldo, segs, c,
+                                                    nullptr, 0);
     return hipGetLastError();
 }
 

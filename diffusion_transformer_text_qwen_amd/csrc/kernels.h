@@ -127,9 +127,15 @@ struct AttnQ8Layout {
     int64_t nt;
 };
 AttnQ8Layout attn_q8_layout(int64_t T_q, int64_t T_k, int H);
+// with_q = false leaves the Q parts of the buffer unwritten (the attention
+// kernel then quantizes bf16 Q itself: launch_attention_q8 with q_bf16).
 hipError_t launch_attn_quantize(const void* q, const void* k, const void* v, int64_t T_q, int64_t T_k, int H,
-                                int64_t ldq, int64_t ldk, int64_t ldv, void* buf, hipStream_t st);
+                                int64_t ldq, int64_t ldk, int64_t ldv, void* buf, hipStream_t st,
+                                bool with_q = true);
+// q_bf16 != NULL: Q is read as bf16 [T_q, H, 128] (row stride ldq) and
+// quantized in the kernel exactly as the buffer's Q codes would be.
 hipError_t launch_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int H, void* o, int64_t ldo,
-                               const AttnSegs& segs, float sm_scale, hipStream_t st);
+                               const AttnSegs& segs, float sm_scale, hipStream_t st,
+                               const void* q_bf16 = nullptr, int64_t ldq = 0);
 
 }  // namespace dit
