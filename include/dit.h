@@ -292,7 +292,12 @@ typedef struct {
     void* v_cache;              /*   are read, rows [T_k-T_q, T_k) are written by the call */
 } dit_block_io;
 
-/* Workspace the block needs for T_q computed rows (bytes, 256-aligned pieces). */
+/*
+ * Workspace the block needs for T_q computed rows (bytes, 256-aligned pieces):
+ * the intermediate activations, and in the bf16 and W8A8 modes also one region
+ * of w8a8_linear_workspace_bytes() for K-split partial sums of the linears
+ * (int32 for W8A8, fp32 for bf16).  Contents need not be initialized.
+ */
 size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k);
 
 /*
