@@ -57,64 +57,83 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict_
     }
 }
 
-// One wave per bf16 row (four rows per workgroup), for K <= 512 * MAXC: the
-// row stays in registers as packed bf16 pairs, reductions are DPP-only, so
-// waves never wait on each other and the whole grid is resident at once for
-// the block's widths.  Same codes and scales as quantize_rows_kernel.
-template <int MAXC, bool GELU_PRE>
-__global__ void __launch_bounds__(256) quantize_rows_wave_kernel(const __bf16* __restrict__ x, int64_t M,
-                                                                 int K, int64_t ldx, int8_t* __restrict__ q,
-                                                                 float* __restrict__ scale) {
+// One workgroup of NW waves per bf16 row, for K <= 512 * NW * C: each lane
+// holds C 16-byte chunks as packed bf16 pairs (chunk (i*NW + w)*64 + lane, so
+// every load and store instruction of a wave covers consecutive bytes), the
+// amax is a DPP wave reduction plus one LDS exchange across the NW waves.
+// Few registers per lane keep eight waves per SIMD resident and the grid is
+// many times the resident set, so workgroups drift out of phase and one's
+// loads overlap another's arithmetic (the GELU variant is VALU-heavy: two
+// transcendentals per element).  Chunks past K read zero and are not stored.
+// Same codes and scales as quantize_rows_kernel.
+template <int NW, int C, bool GELU_PRE>
+__global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16* __restrict__ x, int K,
+                                                                   int64_t ldx, int8_t* __restrict__ q,
+                                                                   float* __restrict__ scale) {
+    __shared__ float red[NW];
     const int lane = threadIdx.x % kWave;
-    // wave-uniform row (an SGPR): buffer resources built from it then need no
-    // per-lane waterfall loop around each load and store
-    const int64_t row = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
-    if (row >= M) return;
+    const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
+    const int64_t row = blockIdx.x;
     const auto xr = raw_rsrc(x + row * ldx, K * 2);
-    v4i buf[MAXC];
+    v4i buf[C];
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) buf[i] = buf_load16(xr, (i * kWave + lane) * 16);
+    for (int i = 0; i < C; ++i) buf[i] = buf_load16(xr, ((i * NW + w) * kWave + lane) * 16);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i)
+    for (int i = 0; i < C; ++i)
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            float lo = bf_lo(buf[i][w]), hi = bf_hi(buf[i][w]);
+        for (int e = 0; e < 4; ++e) {
+            float lo = bf_lo(buf[i][e]), hi = bf_hi(buf[i][e]);
             if constexpr (GELU_PRE) {
-                lo = gelu_tanh_fast(lo);
-                hi = gelu_tanh_fast(hi);
-                buf[i][w] = bf_pack(lo, hi);
-                lo = bf_lo(buf[i][w]);
-                hi = bf_hi(buf[i][w]);
+                buf[i][e] = bf_pack(gelu_tanh_fast(lo), gelu_tanh_fast(hi));
+                lo = bf_lo(buf[i][e]);
+                hi = bf_hi(buf[i][e]);
             }
             amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
         }
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) opaque(buf[i]);
+    for (int i = 0; i < C; ++i) opaque(buf[i]);
     amax = wave_allmax(amax);
+    if (lane == 0) red[w] = amax;
+    __syncthreads();
+    amax = red[0];
+#pragma unroll
+    for (int j = 1; j < NW; ++j) amax = fmaxf(amax, red[j]);
     const float s = __fdiv_rn(amax, 127.0f);
-    if (lane == 0) scale[row] = s;
+    if (threadIdx.x == 0) scale[row] = s;
     const float inv = __fdiv_rn(1.0f, s);
     const bool fast = s >= 0x1p-100f;
     const auto qr = raw_rsrc(q + row * K, K);
 #pragma unroll
-    for (int i = 0; i < MAXC; ++i) {
+    for (int i = 0; i < C; ++i) {
         float v[8];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            v[2 * w] = bf_lo(buf[i][w]);
-            v[2 * w + 1] = bf_hi(buf[i][w]);
+        for (int e = 0; e < 4; ++e) {
+            v[2 * e] = bf_lo(buf[i][e]);
+            v[2 * e + 1] = bf_hi(buf[i][e]);
         }
-        buf_store8(quant8(v, s, inv, fast), qr, (i * kWave + lane) * 8);
+        buf_store8(quant8(v, s, inv, fast), qr, ((i * NW + w) * kWave + lane) * 8);
     }
+}
+
+// Rows of width K <= 16384 through the workgroup-per-row kernel: four waves
+// of two chunks up to 4096 columns, eight waves of four chunks beyond.
+template <bool GELU_PRE>
+static void launch_rows_wg(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* scale,
+                           hipStream_t st) {
+    if (K <= 4096)
+        quantize_rows_wg_kernel<4, 2, GELU_PRE><<<dim3((unsigned)M), dim3(256), 0, st>>>(
+            (const __bf16*)x, (int)K, ldx, q, scale);
+    else
+        quantize_rows_wg_kernel<8, 4, GELU_PRE><<<dim3((unsigned)M), dim3(512), 0, st>>>(
+            (const __bf16*)x, (int)K, ldx, q, scale);
 }
 
 hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
                                 int8_t* q, float* scale, hipStream_t st) {
     if (M == 0) return hipSuccess;
-    if (bf16 && K <= 4096) {
-        quantize_rows_wave_kernel<8, false><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
-            (const __bf16*)x, M, (int)K, ldx, q, scale);
+    if (bf16 && K <= 16384) {
+        launch_rows_wg<false>(x, M, K, ldx, q, scale, st);
         return hipGetLastError();
     }
     if (bf16) {
@@ -141,8 +160,7 @@ hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t
                                      hipStream_t st) {
     if (M == 0) return hipSuccess;
     if (K <= 16384) {
-        quantize_rows_wave_kernel<32, true><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
-            (const __bf16*)u, M, (int)K, K, q, scale);
+        launch_rows_wg<true>(u, M, K, K, q, scale, st);
         return hipGetLastError();
     }
     if (K / 8 <= 256 * 4)
