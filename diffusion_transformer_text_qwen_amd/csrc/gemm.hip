@@ -17,9 +17,20 @@ __device__ __forceinline__ float gelu_tanh(float u) { return gelu_tanh_fast(u); 
 // Epilogue variants, fixed per kernel instantiation (keeps one path live).
 enum EpiVariant : int { EV_STORE = 0, EV_STORE_ACC = 1, EV_GELU = 2, EV_RESID = 3, EV_QKV = 4 };
 
-// EPI_QKV_ROPE, first half, on 16 consecutive columns n..n+15 of one row: bias
-// and the bf16 rounding of the stored QKV output; returns their sum of squares
-// (the row's RMSNorm statistic over its head is the sum over 8 such groups).
+// EPI_QKV_ROPE, first half, on 16 consecutive columns n..n+15 of one row
+// (bias already added): the bf16 rounding of the stored QKV output; returns
+// the sum of squares of the rounded values (the row's RMSNorm statistic over
+// its head is the sum over 8 such groups).
+__device__ __forceinline__ float qkv_stat16(float (&v)[16]) {
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        v[e] = bf16r(v[e]);
+        ss += v[e] * v[e];
+    }
+    return ss;
+}
+// The same, adding the column bias read from memory first.
 __device__ __forceinline__ float qkv_prep16(const EpiParams& ep, int64_t n, float (&v)[16]) {
     if (ep.bias) {
 #pragma unroll
@@ -28,13 +39,7 @@ __device__ __forceinline__ float qkv_prep16(const EpiParams& ep, int64_t n, floa
             v[4 * q] += b.x; v[4 * q + 1] += b.y; v[4 * q + 2] += b.z; v[4 * q + 3] += b.w;
         }
     }
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        v[e] = bf16r(v[e]);
-        ss += v[e] * v[e];
-    }
-    return ss;
+    return qkv_stat16(v);
 }
 
 // Gains and RoPE factors of 16 consecutive columns n..n+15 of row m (loaded
@@ -578,7 +583,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     // waits on a global load of its own.
     constexpr int NPASS = 16 / RPP;
     float colw[16], colb[16], rows_sa[MF][NPASS];
-    if constexpr (EV != EV_QKV) {
+    {
         const bool cb = part == nullptr && n < N && ep.bias != nullptr;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -634,9 +639,6 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             float v[16];
             int32_t ai[16];
             const bool ok = m < M && n < N;
-            if constexpr (EV == EV_QKV) {
-                if (ok) qkv_rope16(ep, m, n, aux);
-            }
             if (ok) {
                 if constexpr (I8) {
                     const float sa = rows_sa[i][pass];
@@ -645,19 +647,10 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
                         // (zero-point correction, if any, is already in the accumulators)
                         const v4i t = *reinterpret_cast<const v4i*>(
                             reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                        if constexpr (EV == EV_QKV) {
-                            const v4f sw = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                ai[4 * q + e] = t[e];
-                                v[4 * q + e] = (float)t[e] * sa * sw[e];
-                            }
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                ai[4 * q + e] = t[e];
-                                v[4 * q + e] = (float)t[e] * sa * colw[4 * q + e];
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            ai[4 * q + e] = t[e];
+                            v[4 * q + e] = (float)t[e] * sa * colw[4 * q + e];
                         }
                     }
                 } else {
@@ -673,11 +666,19 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             }
             if constexpr (EV == EV_QKV) {
                 // a head's 128 columns are this wave's 8 lanes of the row
-                float ss = ok ? qkv_prep16(ep, n, v) : 0.0f;
+                float ss = 0.0f;
+                if (ok) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[e] += colb[e];
+                    ss = qkv_stat16(v);
+                }
                 ss += dpp_f<0xB1>(ss);
                 ss += dpp_f<0x4E>(ss);
                 ss += __shfl_xor(ss, 4, kWave);
-                if (ok) qkv_finish16(ep, m, n, v, ss, aux);
+                if (ok) {
+                    qkv_rope16(ep, m, n, aux);
+                    qkv_finish16(ep, m, n, v, ss, aux);
+                }
             } else {
                 if (ok) {
 #pragma unroll
