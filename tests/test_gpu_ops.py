@@ -13,8 +13,12 @@ from gpu_helpers import DEV, bf16_ulp, dev, host, rel_l2, say
 pytestmark = pytest.mark.gpu
 
 
+# bf16 widths: up to 16384 columns the row's chunks are dealt once over 4 waves
+# (K <= 4096) or 8 (widths that are not whole multiples leave chunks past K);
+# above that one 256-thread workgroup per row strides over the row.
 @pytest.mark.parametrize("M,K,bf16,zero_rows", [
-    (1, 64, True, ()), (37, 4096, True, (3, 36)), (300, 16384, True, (0,)), (5, 512, False, ()),
+    (1, 64, True, ()), (9, 2056, True, ()), (37, 4096, True, (3, 36)), (33, 4104, True, (5,)),
+    (20, 12288, True, ()), (300, 16384, True, (0,)), (6, 24576, True, (2,)), (5, 512, False, ()),
     (64, 16384, False, (1,))])
 def test_quantize_rows_bit_exact(M, K, bf16, zero_rows):
     say("quantize", M, K, bf16)
@@ -26,6 +30,23 @@ def test_quantize_rows_bit_exact(M, K, bf16, zero_rows):
     dq.quantize_rows(dev(x, torch.bfloat16 if bf16 else torch.float32), q, s)
     torch.cuda.synchronize()
     q_ref, s_ref = oracle.quantize_rows(x.astype(np.float64))
+    assert np.array_equal(s.cpu().numpy(), s_ref)
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+@pytest.mark.parametrize("K", [4096, 12296])
+def test_quantize_rows_strided_bit_exact(K):
+    """Rows read with a stride larger than K (a column slice of a wider matrix)."""
+    say("quantize strided", K)
+    M = 11
+    wide = ditsynth.rows(M, K + 64, seed=K + 7, scale=2.0, bf16=True, zero_rows=())
+    x = dev(wide, torch.bfloat16)[:, :K]
+    assert x.stride(0) == K + 64
+    q = torch.empty((M, K), dtype=torch.int8, device=DEV)
+    s = torch.empty(M, dtype=torch.float32, device=DEV)
+    dq.quantize_rows(x, q, s)
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantize_rows(wide[:, :K].astype(np.float64))
     assert np.array_equal(s.cpu().numpy(), s_ref)
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
