@@ -59,7 +59,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* base, in
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                  const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int T_q, int T_k,
-                 int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2) {
+                 int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2, int H) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KS_BYTES + 2 * VT_BYTES];
     uint8_t* const kbuf0 = lds;
     uint8_t* const kbuf1 = lds + KS_BYTES;
@@ -67,8 +67,11 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
     uint8_t* const vbuf1 = lds + 2 * KS_BYTES + VT_BYTES;
 
     const int nqb = (T_q + AQ - 1) / AQ;
-    const int qb = nqb - 1 - (int)blockIdx.x;   // longest key ranges first
-    const int h = blockIdx.y;
+    // one flat grid, head fastest: the longest key ranges of every head go
+    // first, and workgroups are dealt round-robin to the 8 XCDs, so with H a
+    // multiple of 8 all query blocks of a head share one XCD's L2 for its K/V
+    const int qb = nqb - 1 - (int)(blockIdx.x / (unsigned)H);
+    const int h = (int)(blockIdx.x % (unsigned)H);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int hh = lane / 32, lq = lane % 32;
     const int off = T_k - T_q;
@@ -316,10 +319,10 @@ hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, vo
                                  int64_t ldo, const AttnSegs& segs, float sm_scale, hipStream_t st) {
     if (T_q == 0) return hipSuccess;
     const float c = sm_scale * 1.4426950408889634f;
-    dim3 grid((unsigned)((T_q + AQ - 1) / AQ), (unsigned)H);
+    const dim3 grid((unsigned)(((T_q + AQ - 1) / AQ) * H));
     attn_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                                            (__bf16*)o, (int)T_q, (int)T_k, (int)ldq, (int)ldk, (int)ldv,
-                                           (int)ldo, segs, c);
+                                           (int)ldo, segs, c, H);
     return hipGetLastError();
 }
 
