@@ -59,7 +59,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* base, in
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                  const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int T_q, int T_k,
-                 int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2, int H) {
+                 int ldq, int ldk, int ldv, int ldo, AttnSegs sg, float c_log2, int H, int hg) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * KS_BYTES + 2 * VT_BYTES];
     uint8_t* const kbuf0 = lds;
     uint8_t* const kbuf1 = lds + KS_BYTES;
@@ -67,11 +67,8 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
     uint8_t* const vbuf1 = lds + 2 * KS_BYTES + VT_BYTES;
 
     const int nqb = (T_q + AQ - 1) / AQ;
-    // one flat grid, head fastest: the longest key ranges of every head go
-    // first, and workgroups are dealt round-robin to the 8 XCDs, so with H a
-    // multiple of 8 all query blocks of a head share one XCD's L2 for its K/V
-    const int qb = nqb - 1 - (int)(blockIdx.x / (unsigned)H);
-    const int h = (int)(blockIdx.x % (unsigned)H);
+    int qb, h;
+    attn_block_order(blockIdx.x, nqb, H, hg, qb, h);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int hh = lane / 32, lq = lane % 32;
     const int off = T_k - T_q;
@@ -322,7 +319,7 @@ hipError_t launch_attention_bf16(const void* q, const void* k, const void* v, vo
     const dim3 grid((unsigned)(((T_q + AQ - 1) / AQ) * H));
     attn_bf16_kernel<<<grid, 256, 0, st>>>((const __bf16*)q, (const __bf16*)k, (const __bf16*)v,
                                            (__bf16*)o, (int)T_q, (int)T_k, (int)ldq, (int)ldk, (int)ldv,
-                                           (int)ldo, segs, c, H);
+                                           (int)ldo, segs, c, H, attn_head_group(2 * T_k * H * 128 * 2, H));
     return hipGetLastError();
 }
 

@@ -246,16 +246,14 @@ __global__ void __launch_bounds__(256, 2)
 attn_q8_kernel(const int8_t* __restrict__ Q8, const float* __restrict__ SQ, const uint8_t* __restrict__ K8,
                const float* __restrict__ SK, const uint8_t* __restrict__ V8, const float* __restrict__ SV,
                __bf16* __restrict__ O, int T_q, int T_k, int nt, int ldo, AttnSegs sg, float c_log2,
-               const __bf16* __restrict__ QB, int64_t ldqb, int H) {
+               const __bf16* __restrict__ QB, int64_t ldqb, int H, int hg) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[Q8_SLOTS * Q8_SLOT];
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     typedef int v8i __attribute__((ext_vector_type(8)));
 
     const int nqb = (T_q + Q8_QB - 1) / Q8_QB;
-    // one flat grid, head fastest (as in the bf16 kernel): longest key ranges
-    // of every head first, each head's query blocks on one XCD when H % 8 == 0
-    const int qb = nqb - 1 - (int)(blockIdx.x / (unsigned)H);
-    const int h = (int)(blockIdx.x % (unsigned)H);
+    int qb, h;
+    attn_block_order(blockIdx.x, nqb, H, hg, qb, h);
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int hh = lane / 32, lq = lane % 32;
     const int off = T_k - T_q;
@@ -562,17 +560,18 @@ hipError_t launch_attention_q8(const void* buf, int64_t T_q, int64_t T_k, int H,
     const uint8_t* b = (const uint8_t*)buf;
     const float c = sm_scale * 1.4426950408889634f;
     const dim3 grid((unsigned)(((T_q + Q8_QB - 1) / Q8_QB) * H));
+    const int hg = attn_head_group(2 * T_k * H * 128, H);   // int8 K, fp8 V
     if (q_bf16)
         attn_q8_kernel<true><<<grid, 256, 0, st>>>(nullptr, nullptr, (const uint8_t*)(b + L.k8),
                                                    (const float*)(b + L.sk), (const uint8_t*)(b + L.v8),
                                                    (const float*)(b + L.sv), (__bf16*)o, (int)T_q, (int)T_k,
-                                                   (int)L.nt, (int)ldo, segs, c, (const __bf16*)q_bf16, ldq, H);
+                                                   (int)L.nt, (int)ldo, segs, c, (const __bf16*)q_bf16, ldq, H, hg);
     else
         attn_q8_kernel<false><<<grid, 256, 0, st>>>((const int8_t*)(b + L.q8), (const float*)(b + L.sq),
                                                     (const uint8_t*)(b + L.k8), (const float*)(b + L.sk),
                                                     (const uint8_t*)(b + L.v8), (const float*)(b + L.sv),
                                                     (__bf16*)o, (int)T_q, (int)T_k, (int)L.nt, (int)ldo, segs, c,
-                                                    nullptr, 0, H);
+                                                    nullptr, 0, H, hg);
     return hipGetLastError();
 }
 

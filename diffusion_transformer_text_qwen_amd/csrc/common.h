@@ -115,6 +115,25 @@ __device__ __forceinline__ float gelu_tanh_fast(float u) {
     return u * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// Attention work order over one flat grid of nqb query blocks x H heads.
+// Heads go in groups of hg, one group after the other; inside a group the head
+// varies fastest and the query blocks with the longest key ranges come first.
+// Workgroups are dealt round-robin to the 8 XCDs, so with hg a multiple of 8
+// every query block of a head runs on the same XCD (its K/V stay in one L2).
+// The host picks hg = H when the K/V of all heads fit well inside the
+// memory-side cache, else 8, so that only about one group's K/V are live.
+__device__ __forceinline__ void attn_block_order(unsigned b, int nqb, int H, int hg, int& qb, int& h) {
+    const unsigned gsz = (unsigned)(hg * nqb);
+    const int g = (int)(b / gsz), r = (int)(b % gsz);
+    const int h0 = g * hg, cnt = H - h0 < hg ? H - h0 : hg;
+    h = h0 + r % cnt;
+    qb = nqb - 1 - r / cnt;
+}
+// Heads per group for K/V operands of kv_bytes in total.
+inline int attn_head_group(int64_t kv_bytes, int H) {
+    return kv_bytes <= ((int64_t)128 << 20) ? H : (H < 8 ? H : 8);
+}
+
 // Symmetric int8 code of v for scale s (s == 0 -> 0); IEEE fp32 division,
 // ties to even.
 __device__ __forceinline__ int8_t quant_code(float v, float s) {
