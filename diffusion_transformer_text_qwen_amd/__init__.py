@@ -73,6 +73,10 @@ _SIGS = {
     "dit_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "dit_last_error": ([], ctypes.c_char_p),
     "dit_quantize_rows": ([_vp, ctypes.c_int, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp], ctypes.c_int),
+    "dit_gelu_quantize_rows": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp, _vp], ctypes.c_int),
+    "dit_qkv_linear_workspace_bytes": ([_c_i64, _c_i32], ctypes.c_size_t),
+    "dit_qkv_linear": ([ctypes.c_int, _vp, _vp, _c_i64, _c_i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _fp, _vp, _vp,
+                        _vp, _vp, ctypes.c_size_t, _vp], ctypes.c_int),
     "w8a8_linear_workspace_bytes": ([], ctypes.c_size_t),
     "w8a8_linear": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp, _vp,
                      ctypes.c_size_t, _vp], ctypes.c_int),
@@ -170,6 +174,29 @@ def quantize_rows(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor, stream=
     M, K = x.shape
     _check(lib().dit_quantize_rows(_p(x), _dt(x), M, K, x.stride(0), _p(q), _p(scale), _stream(stream)),
            "dit_quantize_rows")
+
+
+def gelu_quantize_rows(u, q, scale, g_out=None, stream=None) -> None:
+    """Codes of g = bf16(GELU_tanh(u)) per row (u bf16 [M, K]); g_out receives g if given."""
+    M, K = u.shape
+    _check(lib().dit_gelu_quantize_rows(_p(u), M, K, u.stride(0), _p(q), _p(scale), _p(g_out), _stream(stream)),
+           "dit_gelu_quantize_rows")
+
+
+def qkv_linear_workspace_bytes(T: int, H: int) -> int:
+    return int(lib().dit_qkv_linear_workspace_bytes(T, H))
+
+
+def qkv_linear(a, w, bias, g_q, g_k, cos_t, sin_t, q_out, k_out, v_out, workspace, a_scale=None, w_scale=None,
+               eps: float = 1e-6, stream=None) -> None:
+    """The block's QKV linear with the fused Q/K RMSNorm + RoPE epilogue: a [T, D]
+    int8 codes (with a_scale, w int8 + w_scale) or bf16; q/k/v_out bf16 [T, D]."""
+    T, D = a.shape
+    mode = MODE_W8A8 if a.dtype == torch.int8 else MODE_BF16
+    _check(lib().dit_qkv_linear(mode, _p(a), _p(a_scale), T, D // 128, _p(w), _p(w_scale), _p(bias), _p(g_q),
+                                _p(g_k), _p(cos_t), _p(sin_t), eps, _p(q_out), _p(k_out), _p(v_out),
+                                _p(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "dit_qkv_linear")
 
 
 def quantize_rows_asym(x, q, scale, zero, stream=None) -> None:

@@ -153,6 +153,21 @@ int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t 
     return DIT_OK;
 }
 
+int dit_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int64_t ldu, int8_t* q, float* scale,
+                           void* g_out, void* stream) {
+    CHECK(M >= 0 && K >= 1 && ldu >= K, DIT_E_SHAPE, "need M>=0, K>=1, ldu>=K");
+    CHECK(K % 8 == 0 && ldu % 8 == 0, DIT_E_UNSUPPORTED, "K and ldu must be multiples of 8");
+    CHECK(K <= 16384, DIT_E_UNSUPPORTED, "K=%lld above 16384", (long long)K);
+    CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
+    CHECK(ldu * 2 * (M ? M : 1) < ((int64_t)1 << 62), DIT_E_UNSUPPORTED, "u too large");
+    if (M == 0) return DIT_OK;
+    CHECK(u && q && scale, DIT_E_NULL, "u, q and scale must be non-NULL");
+    CHECK(aligned16(u) && aligned16(q) && (!g_out || aligned16(g_out)), DIT_E_ALIGN,
+          "u, q and g_out must be 16-byte aligned");
+    RUN(launch_gelu_quantize_rows(u, M, K, q, scale, S(stream), ldu, g_out), "gelu_quantize_rows");
+    return DIT_OK;
+}
+
 size_t w8a8_linear_workspace_bytes(void) { return (size_t)kSplitPartialBytes; }
 
 int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
@@ -307,6 +322,53 @@ int f32_linear(const float* a, int64_t M, int64_t K, int64_t lda, const float* w
     return DIT_OK;
 }
 
+size_t dit_qkv_linear_workspace_bytes(int64_t T, int32_t H) {
+    if (T < 0 || H < 1) return 0;
+    return (size_t)kSplitPartialBytes + (((size_t)T * 3 * H * 128 * 2 + 255) & ~(size_t)255);
+}
+
+int dit_qkv_linear(int mode, const void* a, const float* a_scale, int64_t T, int32_t H, const void* w,
+                   const float* w_scale, const float* bias, const float* g_q, const float* g_k, const float* cos_t,
+                   const float* sin_t, float eps, void* q_out, void* k_out, void* v_out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    CHECK(mode == DIT_MODE_BF16 || mode == DIT_MODE_W8A8, DIT_E_DTYPE, "mode must be BF16 or W8A8");
+    CHECK(T >= 0 && H >= 1, DIT_E_SHAPE, "need T>=0, H>=1");
+    const int64_t D = (int64_t)H * 128;
+    CHECK(D % 256 == 0 && D <= 8192, DIT_E_UNSUPPORTED, "H*128 must be a multiple of 256, <= 8192");
+    CHECK(T * 3 * D < ((int64_t)1 << 31), DIT_E_UNSUPPORTED, "T * 3 * H * 128 must be below 2^31");
+    CHECK(eps >= 0.0f, DIT_E_SHAPE, "eps must be >= 0");
+    CHECK(workspace != nullptr && workspace_bytes >= dit_qkv_linear_workspace_bytes(T, H), DIT_E_WORKSPACE,
+          "workspace needs %zu bytes", dit_qkv_linear_workspace_bytes(T, H));
+    if (T == 0) return DIT_OK;
+    CHECK(a && w && g_q && g_k && cos_t && sin_t && q_out && k_out && v_out, DIT_E_NULL, "NULL argument");
+    CHECK(mode != DIT_MODE_W8A8 || (a_scale && w_scale), DIT_E_NULL, "W8A8 needs a_scale and w_scale");
+    CHECK(aligned16(a) && aligned16(w) && aligned16(g_q) && aligned16(g_k) && aligned16(cos_t) &&
+              aligned16(sin_t) && aligned16(q_out) && aligned16(k_out) && aligned16(v_out) &&
+              aligned16(workspace) && (!bias || aligned16(bias)),
+          DIT_E_ALIGN, "pointers must be 16-byte aligned");
+    EpiParams ep = store_epi((uint8_t*)workspace + kSplitPartialBytes, 3 * D, true, bias);
+    ep.kind = EPI_QKV_ROPE;
+    ep.q_out = q_out;
+    ep.k_out = k_out;
+    ep.v_out = v_out;
+    ep.g_q = g_q;
+    ep.g_k = g_k;
+    ep.cos_t = cos_t;
+    ep.sin_t = sin_t;
+    ep.qk_eps = eps;
+    ep.D = D;
+    ep.split_partial = (int32_t*)workspace;
+    ep.split_bytes = kSplitPartialBytes;
+    if (mode == DIT_MODE_W8A8) {
+        ep.a_scale = a_scale;
+        ep.w_scale = w_scale;
+        RUN(launch_gemm_i8((const int8_t*)a, (const int8_t*)w, T, 3 * D, D, ep, S(stream)), "qkv_linear");
+    } else {
+        RUN(launch_gemm_bf16(a, D, w, T, 3 * D, D, ep, S(stream)), "qkv_linear");
+    }
+    return DIT_OK;
+}
+
 int block_causal_attention(const void* q, const void* k, const void* v, void* o, int dtype, int64_t T_q,
                            int64_t T_k, int32_t H, int32_t d, int64_t ldq, int64_t ldk, int64_t ldv,
                            int64_t ldo, const int32_t* seg_len, int32_t n_seg, float sm_scale,
@@ -382,14 +444,16 @@ int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const f
                        const float* scale, float eps, void* h_out, int h_dtype, int8_t* q_out,
                        float* q_scale, void* stream) {
     CHECK(x_dtype == DIT_BF16 || x_dtype == DIT_F32, DIT_E_DTYPE, "x_dtype must be bf16 or f32");
-    CHECK(q_out != nullptr || h_dtype == x_dtype, DIT_E_DTYPE, "h_dtype must equal x_dtype");
+    CHECK(h_out == nullptr || h_dtype == x_dtype, DIT_E_DTYPE, "h_dtype must equal x_dtype");
     CHECK(M >= 0 && D >= 256, DIT_E_SHAPE, "need M>=0, D>=256");
     CHECK(D % 256 == 0 && D <= 8192, DIT_E_UNSUPPORTED, "D must be a multiple of 256, <= 8192");
     CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
     if (M == 0) return DIT_OK;
     CHECK(x && shift && scale, DIT_E_NULL, "x, shift and scale must be non-NULL");
-    CHECK(q_out ? (q_scale != nullptr) : (h_out != nullptr), DIT_E_NULL, "output pointer is NULL");
-    CHECK(aligned16(x) && (!q_out || aligned16(q_out)), DIT_E_ALIGN, "x and q_out must be 16-byte aligned");
+    CHECK(h_out != nullptr || q_out != nullptr, DIT_E_NULL, "h_out and q_out are both NULL");
+    CHECK(q_out == nullptr || q_scale != nullptr, DIT_E_NULL, "q_scale is NULL");
+    CHECK(aligned16(x) && (!q_out || aligned16(q_out)) && (!h_out || aligned16(h_out)), DIT_E_ALIGN,
+          "x, h_out and q_out must be 16-byte aligned");
     SegMap sm{};
     sm.end[0] = M;
     sm.set[0] = 0;
@@ -540,9 +604,13 @@ int check_weights(const dit_block_config* cfg, const dit_block_weights* w) {
 int check_io(const dit_block_config* cfg, const dit_block_io* io) {
     CHECK(io != nullptr, DIT_E_NULL, "io is NULL");
     CHECK(io->T_q >= 0 && io->T_q <= io->T_k, DIT_E_SHAPE, "need 0 <= T_q <= T_k");
-    CHECK(io->T_k <= ((int64_t)1 << 31), DIT_E_UNSUPPORTED, "T_k too large");
+    CHECK(io->T_k < ((int64_t)1 << 31), DIT_E_UNSUPPORTED, "T_k must be below 2^31");
     int s = check_segs(io->seg_len, io->n_seg, io->T_k);
     if (s) return s;
+    if (cfg->attn_quant) {
+        s = check_q8_shape(io->T_q, io->T_k, cfg->H);
+        if (s) return s;
+    }
     CHECK(io->n_mod >= 1, DIT_E_SHAPE, "n_mod must be >= 1");
     CHECK(io->mod_of_seg != nullptr, DIT_E_NULL, "mod_of_seg is NULL");
     for (int i = 0; i < io->n_seg; ++i)
@@ -553,7 +621,6 @@ int check_io(const dit_block_config* cfg, const dit_block_io* io) {
           "x, mod, cos_t, sin_t, k_cache and v_cache must be non-NULL");
     CHECK(aligned16(io->x) && aligned16(io->k_cache) && aligned16(io->v_cache), DIT_E_ALIGN,
           "x and the caches must be 16-byte aligned");
-    (void)cfg;
     return DIT_OK;
 }
 
@@ -608,7 +675,8 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     // S1: adaLN prologue 1 (fused per-token quantization in W8A8 mode)
     {
     ProfScope ps(DIT_SITE_ADALN1, st);
-    RUN(launch_adaln(x, bf, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
+    RUN(launch_adaln(x, bf, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, q8 ? nullptr : h,
+                     q8 ? a8 : nullptr, sa, st),
         "adaln1");
     }
     // S2 + S3: QKV linear; Q/K RMSNorm + RoPE and the K/V cache rows.  In the
@@ -679,7 +747,8 @@ int block_impl(const dit_block_config* cfg, const dit_block_weights* w, const di
     // S7: adaLN prologue 2
     {
     ProfScope ps(DIT_SITE_ADALN2, st);
-    RUN(launch_adaln(x, bf, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, q8 ? a8 : nullptr, sa, st),
+    RUN(launch_adaln(x, bf, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, q8 ? nullptr : h,
+                     q8 ? a8 : nullptr, sa, st),
         "adaln2");
     }
     // S8: MLP up + GELU.  W8A8: the up GEMM stores u (bf16) and the GELU is

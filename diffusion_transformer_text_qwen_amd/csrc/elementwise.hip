@@ -69,7 +69,8 @@ __global__ void __launch_bounds__(256) quantize_rows_kernel(const T* __restrict_
 template <int NW, int C, bool GELU_PRE>
 __global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16* __restrict__ x, int K,
                                                                    int64_t ldx, int8_t* __restrict__ q,
-                                                                   float* __restrict__ scale) {
+                                                                   float* __restrict__ scale,
+                                                                   __bf16* __restrict__ g_out) {
     __shared__ float red[NW];
     const int lane = threadIdx.x % kWave;
     const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x / kWave));
@@ -93,6 +94,12 @@ __global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16*
         }
 #pragma unroll
     for (int i = 0; i < C; ++i) opaque(buf[i]);
+    if (GELU_PRE && g_out != nullptr) {
+        // the bf16 GELU values the codes are taken from (parity checks)
+        const auto gr = raw_rsrc(g_out + row * K, K * 2);
+#pragma unroll
+        for (int i = 0; i < C; ++i) buf_store16(buf[i], gr, ((i * NW + w) * kWave + lane) * 16);
+    }
     amax = wave_allmax(amax);
     if (lane == 0) red[w] = amax;
     __syncthreads();
@@ -120,13 +127,13 @@ __global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16*
 // of two chunks up to 4096 columns, eight waves of four chunks beyond.
 template <bool GELU_PRE>
 static void launch_rows_wg(const void* x, int64_t M, int64_t K, int64_t ldx, int8_t* q, float* scale,
-                           hipStream_t st) {
+                           hipStream_t st, void* g_out = nullptr) {
     if (K <= 4096)
         quantize_rows_wg_kernel<4, 2, GELU_PRE><<<dim3((unsigned)M), dim3(256), 0, st>>>(
-            (const __bf16*)x, (int)K, ldx, q, scale);
+            (const __bf16*)x, (int)K, ldx, q, scale, (__bf16*)g_out);
     else
         quantize_rows_wg_kernel<8, 4, GELU_PRE><<<dim3((unsigned)M), dim3(512), 0, st>>>(
-            (const __bf16*)x, (int)K, ldx, q, scale);
+            (const __bf16*)x, (int)K, ldx, q, scale, (__bf16*)g_out);
 }
 
 hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, int64_t ldx,
@@ -157,12 +164,14 @@ hipError_t launch_quantize_rows(const void* x, bool bf16, int64_t M, int64_t K, 
 }
 
 hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
-                                     hipStream_t st) {
+                                     hipStream_t st, int64_t ldu, void* g_out) {
     if (M == 0) return hipSuccess;
+    if (ldu == 0) ldu = K;
     if (K <= 16384) {
-        launch_rows_wg<true>(u, M, K, K, q, scale, st);
+        launch_rows_wg<true>(u, M, K, ldu, q, scale, st, g_out);
         return hipGetLastError();
     }
+    if (g_out != nullptr || ldu != K) return hipErrorInvalidValue;
     if (K / 8 <= 256 * 4)
         quantize_rows_kernel<__bf16, 4, true><<<dim3((unsigned)M), dim3(256), 0, st>>>(
             (const __bf16*)u, K, K, q, scale);
@@ -226,7 +235,7 @@ __global__ void __launch_bounds__(256) adaln_kernel(const T* __restrict__ x, int
                 amax = fmaxf(amax, fabsf(hv));
             }
         }
-    if (qo == nullptr) {
+    if (h != nullptr) {
 #pragma unroll
         for (int i = 0; i < VPT / 8; ++i)
             if (i < nvec) {
@@ -234,8 +243,8 @@ __global__ void __launch_bounds__(256) adaln_kernel(const T* __restrict__ x, int
 #pragma unroll
                 for (int e = 0; e < 8; ++e) h[row * D + c + e] = from_f<T>(v[i * 8 + e]);
             }
-        return;
     }
+    if (qo == nullptr) return;
     amax = block_reduce<4, true>(amax, red);
     const float sc = __fdiv_rn(amax, 127.0f);
     if (threadIdx.x == 0) qs[row] = sc;
@@ -313,12 +322,12 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
         }
         opaque(buf[i]);
     }
-    if (qo == nullptr) {
+    if (h != nullptr) {
         const auto hr = raw_rsrc(h + row * D, D * 2);
 #pragma unroll
         for (int i = 0; i < MAXC; ++i) buf_store16(buf[i], hr, (i * kWave + lane) * 16);
-        return;
     }
+    if (qo == nullptr) return;
     amax = wave_allmax(amax);
     const float sq = __fdiv_rn(amax, 127.0f);
     if (lane == 0) qs[row] = sq;
@@ -344,7 +353,7 @@ hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const fl
                         float* qs, hipStream_t st) {
     if (M == 0) return hipSuccess;
     if (bf16 && D % 8 == 0 && D <= 4096 && mod_stride % 4 == 0 && al16(x) && al16(shift) && al16(scale) &&
-        (qo ? ((uintptr_t)qo & 7) == 0 : al16(h))) {
+        (qo == nullptr || ((uintptr_t)qo & 7) == 0) && (h == nullptr || al16(h))) {
         adaln_wave_kernel<8><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
             (const __bf16*)x, M, (int)D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs);
         return hipGetLastError();
@@ -405,14 +414,14 @@ __global__ void __launch_bounds__(256) adaln_small_kernel(const T* __restrict__ 
             amax = fmaxf(amax, fabsf(v[i]));
         }
     }
-    if (qo == nullptr) {
+    if (h != nullptr) {
 #pragma unroll
         for (int i = 0; i < MAXV; ++i) {
             const int64_t c = (int64_t)i * 256 + threadIdx.x;
             if (c < D) h[row * D + c] = from_f<T>(v[i]);
         }
-        return;
     }
+    if (qo == nullptr) return;
     amax = block_reduce<4, true>(amax, red);
     const float sc = __fdiv_rn(amax, 127.0f);
     if (threadIdx.x == 0) qs[row] = sc;

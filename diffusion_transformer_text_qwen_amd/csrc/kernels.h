@@ -77,8 +77,11 @@ hipError_t launch_quantize_rows_asym(const void* x, bool bf16, int64_t M, int64_
 hipError_t launch_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* out,
                                hipStream_t st);
 hipError_t launch_int8_colsum(const int8_t* w, int64_t N, int64_t K, int32_t* out, hipStream_t st);
+// g = bf16(GELU_tanh(u)) of bf16 u [M, K] (row stride ldu, 0 = K), quantized per
+// row; g_out (bf16 [M, K], row stride K) also receives g when not NULL (K <= 16384).
 hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t* q, float* scale,
-                                     hipStream_t st);
+                                     hipStream_t st, int64_t ldu = 0, void* g_out = nullptr);
+// h (if not NULL) and/or the int8 codes of h (qo, qs; if qo is not NULL).
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                         const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
                         float* qs, hipStream_t st);

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 3
+#define DIT_ABI_VERSION 4
 
 typedef enum {
     DIT_OK = 0,
@@ -68,6 +68,20 @@ const char* dit_last_error(void);
  */
 int dit_quantize_rows(const void* x, int x_dtype, int64_t M, int64_t K, int64_t ldx,
                       int8_t* q, float* scale, void* stream);
+
+/*
+ * GELU fused into the per-row quantization of the MLP activation (the W8A8
+ * block's MLP-down input).  g = bf16(GELU_tanh(u)) with the tanh form
+ * 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))) evaluated in fp32
+ * ("qwen-image-mnn" and the Core AI port name a GELU MLP; the tanh form is the
+ * workloads' choice), then the codes of g exactly as dit_quantize_rows.
+ * u [M, K] bf16 (row stride ldu elements); q [M, K] int8 (row stride K); scale
+ * [M] fp32; g_out (NULL or bf16 [M, K], row stride K) also receives g, the
+ * values the codes are taken from.  Supported: K % 8 == 0, ldu % 8 == 0,
+ * K <= 16384, 16-byte aligned u, q and g_out.
+ */
+int dit_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int64_t ldu, int8_t* q, float* scale,
+                           void* g_out, void* stream);
 
 /*
  * W8A8 linear ("Qwen-Image-2.1 W8A8 - FlagOS for Mac", Quantization and
@@ -118,8 +132,10 @@ int w8a8_linear_asym(const int8_t* a, const float* a_scale, const int32_t* a_zer
                      void* y, int y_dtype, int64_t ldy, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * bf16 linear for the non-quantized linears: y = a w^T + bias with fp32
- * accumulation.  a [M, K] bf16 (row stride lda), w [N, K] bf16 (row stride K),
+ * bf16 linear for the non-quantized linears ("Qwen-Image-2.1 W8A8 - FlagOS for
+ * Mac", Quantization and validation: the linears outside the W8A8 set stay
+ * BF16; "qwen-image-mnn", Install / run: no fp16 arithmetic on this path):
+ * y = a w^T + bias with fp32 accumulation.  a [M, K] bf16 (row stride lda), w [N, K] bf16 (row stride K),
  * bias [N] fp32 or NULL, y [M, N] bf16 or fp32 (row stride ldy).
  * Supported: K % 64 == 0, N % 16 == 0, lda % 8 == 0.
  */
@@ -127,12 +143,39 @@ int bf16_linear(const void* a, int64_t M, int64_t K, int64_t lda, const void* w,
                 const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy, void* stream);
 
 /*
- * fp32 linear (fp32 mode): y = a w^T + bias, fp32 throughout.  a [M, K] f32
+ * fp32 linear, the fp32 mode's linears ("Qwen Image 2.1 native qualification",
+ * Numerical checks: the fp32 re-implementation checked against the reference
+ * at fine tolerances): y = a w^T + bias, fp32 throughout.  a [M, K] f32
  * (row stride lda), w [N, K] f32, y [M, N] f32 (row stride ldy).
  * Supported: K % 16 == 0, N % 16 == 0.
  */
 int f32_linear(const float* a, int64_t M, int64_t K, int64_t lda, const float* w,
                const float* bias, int64_t N, float* y, int64_t ldy, void* stream);
+
+/*
+ * The block's QKV linear with its fused epilogue (the path dit_block_forward
+ * runs in the bf16 and W8A8 modes): [q | k | v] = a w^T + bias, rounded to
+ * bf16; per token and 128-wide head of q and k the RMSNorm of
+ * dit_qk_norm_rope with the cast to bf16 before the gain multiply ("Qwen Image
+ * 2.1 native qualification", Numerical checks), then the interleaved RoPE
+ * rotation by cos_t/sin_t [T, 64] ("RGBA-Image-2.1 - Core AI port", Graph
+ * contracts), rounded to bf16; v passes through.
+ * mode DIT_MODE_W8A8: a int8 codes [T, D] with a_scale [T], w int8 [3D, D] with
+ * w_scale [3D] (the linear of w8a8_linear); mode DIT_MODE_BF16: a bf16 [T, D],
+ * w bf16 [3D, D], scales unused.  D = H*128.  bias [3D] fp32 or NULL; g_q, g_k
+ * [128] fp32.  q_out, k_out, v_out: bf16 [T, D] each (row stride D; k_out and
+ * v_out may be the rows [T_k - T, T_k) of a [T_k, H, 128] K/V cache).
+ * workspace: dit_qkv_linear_workspace_bytes(T, H) bytes of device scratch
+ * (K-split partial sums, and the [q|k|v] rows of the launches that store them
+ * before a separate norm/RoPE pass); contents need not be initialized.
+ * Supported: D % 256 == 0, D <= 8192, T * 3D < 2^31; every pointer 16-byte
+ * aligned.
+ */
+size_t dit_qkv_linear_workspace_bytes(int64_t T, int32_t H);
+int dit_qkv_linear(int mode, const void* a, const float* a_scale, int64_t T, int32_t H, const void* w,
+                   const float* w_scale, const float* bias, const float* g_q, const float* g_k, const float* cos_t,
+                   const float* sin_t, float eps, void* q_out, void* k_out, void* v_out, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * Block-causal attention ("RGBA-Image-2.1 - Core AI port", intro; "qwen-image-mnn",
@@ -229,12 +272,14 @@ int dit_qk_norm_rope(const void* qkv, int dtype, int64_t T, int32_t H, const flo
                      void* stream);
 
 /*
- * adaLN prologue: h = LayerNorm(x) * (1 + scale) + shift (no affine, biased
- * variance, fp32 statistics) with one (shift, scale) pair [D] fp32 for all rows.
- * x [M, D] bf16 or f32 (row stride D).  Output either h [M, D] (h_dtype bf16 or
- * f32; bf16 rounds once), or, when q_out is not NULL, the bf16-rounded h
+ * adaLN prologue ("qwen-image-mnn", What runs where: timestep modulation rows
+ * shift and scale the normalized tokens): h = LayerNorm(x) * (1 + scale) + shift
+ * (no affine, biased variance, fp32 statistics) with one (shift, scale) pair [D]
+ * fp32 for all rows.  x [M, D] bf16 or f32 (row stride D).  Outputs (at least
+ * one): h [M, D] when h_out is not NULL (h_dtype must equal x_dtype; bf16
+ * rounds once), and, when q_out is not NULL, that same h (bf16-rounded in bf16)
  * quantized per row as in dit_quantize_rows (q_out [M, D] int8, q_scale [M]).
- * Supported: D % 256 == 0, D <= 8192.
+ * Supported: D % 256 == 0, D <= 8192; x, h_out and q_out 16-byte aligned.
  */
 int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const float* shift,
                        const float* scale, float eps, void* h_out, int h_dtype, int8_t* q_out,
@@ -301,7 +346,12 @@ typedef struct {
 size_t dit_block_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k);
 
 /*
- * One single-stream DiT block on the last T_q rows of a T_k-token sequence:
+ * One single-stream DiT block ("RGBA-Image-2.1 - Core AI port of Qwen-Image-2.1",
+ * intro and Graph contracts: one stream over [text | image] with block-causal
+ * attention; "qwen-image-mnn", What runs where: 3-axis RoPE, Q/K RMSNorm and
+ * the timestep modulation rows; "Qwen-Image-2.1 W8A8 - FlagOS for Mac",
+ * Quantization and validation: the W8A8 linears) on the last T_q rows of a
+ * T_k-token sequence:
  *   h  = LN(x)(1+scale1)+shift1;  [q|k|v] = h Wqkv^T + b_qkv
  *   q, k <- RoPE(RMSNorm(q, k) * g);  K/V rows -> cache
  *   o  = block-causal attention(q, K cache, V cache)   (int8/fp8 if cfg->attn_quant)
@@ -447,7 +497,9 @@ typedef struct {
     void* vel;                  /* [N, C_lat] activation dtype: the velocity */
 } dit_velocity_io;
 
-/* Workspace of dit_velocity_forward (bytes); T_k = L_txt + R + N. */
+/* Workspace of dit_velocity_forward (bytes); T_k = L_txt + R + N.  After a
+ * call the workspace begins with the block stack's output rows x [T_q, D]
+ * (activation dtype, row stride D), the input of the tail. */
 size_t dit_velocity_workspace_bytes(const dit_block_config* cfg, int64_t T_q, int64_t T_k, int64_t N,
                                     int32_t C_lat);
 

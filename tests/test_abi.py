@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dq.exported_symbols())
-    assert lib.dit_abi_version() == 3
+    assert lib.dit_abi_version() == 4
 
 
 def test_status_strings():
@@ -105,6 +105,39 @@ def test_rope_and_misc_validation():
     assert lib.dit_adaln_modulate(16, dq.BF16, 4, 300, 16, 16, 1e-6, 16, dq.BF16, NULL, NULL, S) == 5
     assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 16, dq.F32, NULL, NULL, S) == 3
     assert lib.dit_euler_step(NULL, NULL, dq.F32, 10, 1.0, 0.5, S) == 1
+    # h and codes together; neither is an error; misaligned h
+    assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, NULL, dq.BF16, NULL, NULL, S) == 1
+    assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 24, dq.BF16, 16, 16, S) == 4
+    assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 16, dq.BF16, 16, NULL, S) == 1
+
+
+def test_gelu_quantize_validation():
+    lib = dq.lib()
+    assert lib.dit_gelu_quantize_rows(16, 4, 64, 32, 16, 16, NULL, S) == 2       # ldu < K
+    assert lib.dit_gelu_quantize_rows(16, 4, 60, 64, 16, 16, NULL, S) == 5       # K % 8
+    assert lib.dit_gelu_quantize_rows(16, 4, 16392, 16392, 16, 16, NULL, S) == 5  # K > 16384
+    assert lib.dit_gelu_quantize_rows(16, 4, 64, 64, NULL, 16, NULL, S) == 1
+    assert lib.dit_gelu_quantize_rows(16, 4, 64, 64, 16, 16, 24, S) == 4         # misaligned g_out
+    assert lib.dit_gelu_quantize_rows(NULL, 0, 64, 64, NULL, NULL, NULL, S) == 0
+
+
+def test_qkv_linear_validation():
+    lib = dq.lib()
+    need = lib.dit_qkv_linear_workspace_bytes(4352, 32)
+    assert need >= lib.w8a8_linear_workspace_bytes() + 4352 * 3 * 4096 * 2
+
+    def call(mode=dq.MODE_W8A8, T=8, H=4, ws=256, wsb=1 << 40, ptr=256, scale=256):
+        return lib.dit_qkv_linear(mode, ptr, scale, T, H, ptr, scale, NULL, ptr, ptr, ptr, ptr, 1e-6, ptr, ptr, ptr,
+                                  ws, wsb, S)
+    assert call(mode=dq.MODE_F32) == 3
+    assert call(H=3) == 5                              # D % 256
+    assert call(H=128) == 5                            # D > 8192
+    assert call(ws=NULL) == 6
+    assert call(wsb=1024) == 6
+    assert call(ptr=NULL) == 1
+    assert call(scale=NULL) == 1                       # W8A8 needs scales
+    assert call(mode=dq.MODE_BF16, scale=NULL, ptr=264) == 4
+    assert call(T=0) == 0
 
 
 def _block_args(mode=dq.MODE_W8A8, D=512, H=4, F=2048, segs=(16, 64), T_q=80, mos=(0, 0), n_mod=1):
@@ -148,6 +181,14 @@ def test_block_validation():
     assert call(cfg, w, io) == 1
     cfg, w, io, keep = _block_args()
     assert call(cfg, w, io, ws=256, wsb=1024) == 6     # workspace too small
+    # the kernels take T_k as a 32-bit count
+    cfg, w, io, keep = _block_args(segs=(16, (1 << 31) - 16), T_q=80)
+    assert call(cfg, w, io) == 5
+    # int8/fp8 attention: H * ceil(T_k / 64) * 8192 (the K and V operand images)
+    # must stay below 2^31 bytes (H = 32: T_k < 524288)
+    cfg, w, io, keep = _block_args(D=4096, H=32, F=16384, segs=(16, 600000 - 16), T_q=80)
+    cfg.attn_quant = 1
+    assert call(cfg, w, io) == 5
     cfg, w, io, keep = _block_args()
     io.x = 264
     assert call(cfg, w, io) == 4
