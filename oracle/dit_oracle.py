@@ -495,9 +495,18 @@ def attention_quantized(q, k, v, seg_len: Sequence[int], scale: Optional[float] 
 # ----------------------------------------------------------------------------- MLP
 
 def gelu_tanh(u) -> np.ndarray:
-    """tanh-approximated GELU (the workloads' MLP activation)."""
+    """tanh-approximated GELU (the workloads' MLP activation):
+    0.5 u (1 + tanh(x)) with x = sqrt(2/pi) (u + 0.044715 u^3).
+
+    For x < 0 the factor 1 + tanh(x) is taken as 2 e^{2x} / (1 + e^{2x}), the
+    same number written without the cancellation that leaves fp64's
+    1 + tanh(x) at zero or rounding noise once x < -19 (u below about -6).
+    """
     u = np.asarray(u, np.float64)
-    return 0.5 * u * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)))
+    x = math.sqrt(2.0 / math.pi) * (u + 0.044715 * u ** 3)
+    e = np.exp(2.0 * np.minimum(x, 0.0))
+    one_plus_tanh = np.where(x >= 0.0, 1.0 + np.tanh(np.maximum(x, 0.0)), 2.0 * e / (1.0 + e))
+    return 0.5 * u * one_plus_tanh
 
 
 # ----------------------------------------------------------------------------- block

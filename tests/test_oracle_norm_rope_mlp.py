@@ -134,3 +134,31 @@ def test_gelu_closed_forms_and_library():
     assert np.allclose(g - oracle.gelu_tanh(-u), u, atol=1e-13)         # odd part is x/2
     assert np.isclose(oracle.gelu_tanh(np.array([1.0]))[0],
                       0.5 * (1 + math.tanh(math.sqrt(2 / math.pi) * 1.044715)))
+
+
+def _gelu_decimal(u: float) -> float:
+    """0.5 u (1 + tanh(x)) in 120-digit decimal arithmetic, tanh from its
+    exponential definition (textbook formula, no cancellation at this precision)."""
+    import decimal
+    with decimal.localcontext() as ctx:
+        ctx.prec = 120
+        U = decimal.Decimal(u)
+        k = (decimal.Decimal(2) / decimal.Decimal(math.pi)).sqrt()
+        X = k * (U + decimal.Decimal("0.044715") * U ** 3)
+        e2 = (2 * X).exp()
+        tanh = (e2 - 1) / (e2 + 1)
+        return float(decimal.Decimal("0.5") * U * (1 + tanh))
+
+
+def test_gelu_matches_high_precision_definition_in_the_negative_tail():
+    """Relative error below 1e-12 against the tanh definition evaluated to 120
+    digits (1 + tanh keeps 70 of them at u = -11), including u far enough below zero that fp64 1 + tanh(x) cancels
+    (pi enters through fp64 math.pi in both, so the constant is the same)."""
+    us = [-11.0, -9.5, -8.0, -6.5, -5.0, -3.0, -1.0, -0.25, 0.0, 0.3, 1.7, 4.0, 9.0]
+    got = oracle.gelu_tanh(np.array(us))
+    for u, g in zip(us, got):
+        ref = _gelu_decimal(u)
+        assert abs(g - ref) <= 1e-12 * abs(ref) + 1e-300, (u, g, ref)
+    # the naive fp64 evaluation loses the tail (what the rewritten form avoids)
+    naive = 0.5 * -8.0 * (1.0 + math.tanh(math.sqrt(2 / math.pi) * (-8.0 + 0.044715 * -512.0)))
+    assert naive == 0.0 and _gelu_decimal(-8.0) < 0.0
