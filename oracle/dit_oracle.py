@@ -49,15 +49,24 @@ QK_EPS = 1e-6
 def round_bf16(a) -> np.ndarray:
     """Nearest bfloat16 value of each element (ties to even), as float64.
 
-    bf16 keeps 7 of fp64's 52 explicit mantissa bits; the low 45 bits are
-    rounded off on the integer view.  Valid for finite values in the normal
-    bf16 range, which is all the block produces.
+    bf16 keeps 7 of fp64's 52 explicit mantissa bits; in bf16's normal range
+    (|a| >= 2^-126) the low 45 bits are rounded off on the integer view.  Below
+    it bf16 is subnormal with a fixed step of 2^-133 (fp32's exponent range, 7
+    fraction bits), so the value is rounded to a multiple of that step (values
+    under half a step go to a signed zero).  Valid for finite values below
+    bf16's largest finite value.
     """
     a = np.ascontiguousarray(a, dtype=np.float64)
     bits = a.view(np.uint64)
     lsb = (bits >> np.uint64(45)) & np.uint64(1)
     bits = (bits + np.uint64((1 << 44) - 1) + lsb) & ~np.uint64((1 << 45) - 1)
-    return bits.view(np.float64)
+    out = bits.view(np.float64)
+    tiny = np.abs(a) < 2.0 ** -126
+    if np.any(tiny):
+        out = out.copy()
+        sub = np.rint(a[tiny] * 2.0 ** 133) * 2.0 ** -133   # exact scaling, ties to even
+        out[tiny] = np.copysign(sub, a[tiny])
+    return out
 
 
 def _store(a, mode: str):

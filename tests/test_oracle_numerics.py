@@ -24,6 +24,21 @@ def test_round_bf16_matches_library_rne_on_fp32_inputs():
     assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
 
 
+def test_round_bf16_subnormal_range_matches_library():
+    """fp32 inputs around and below bf16's smallest normal 2^-126 (fp32
+    subnormals included), against torch's fp32 -> bf16 rounding."""
+    rng = np.random.default_rng(12)
+    e = rng.uniform(-152.0, -120.0, 100_000)
+    x = (np.sign(rng.standard_normal(e.size)) * 2.0 ** e).astype(np.float32)
+    u = x.view(np.uint32).copy()
+    u[::5] = (u[::5] & 0xFFFF0000) | 0x8000            # ties
+    x = u.view(np.float32)
+    ref = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x.astype(np.float64))
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
 def test_round_bf16_hand_values():
     r = oracle.round_bf16
     assert r(1.0) == 1.0
