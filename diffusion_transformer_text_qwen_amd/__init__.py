@@ -80,6 +80,8 @@ _SIGS = {
     "w8a8_linear_workspace_bytes": ([], ctypes.c_size_t),
     "w8a8_linear": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp, _vp,
                      ctypes.c_size_t, _vp], ctypes.c_int),
+    "w8a8_linear_noalloc": ([_vp, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp,
+                             _vp], ctypes.c_int),
     "bf16_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, ctypes.c_int, _c_i64, _vp],
                     ctypes.c_int),
     "f32_linear": ([_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _c_i64, _vp], ctypes.c_int),
@@ -245,6 +247,14 @@ def w8a8_linear(a, a_scale, w, w_scale, bias, y, acc_out=None, workspace=None, s
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().w8a8_linear(_p(a), _p(a_scale), M, K, _p(w), _p(w_scale), _p(bias), N, _p(y), _dt(y),
                              y.stride(0), _p(acc_out), _p(workspace), wsb, _stream(stream)), "w8a8_linear")
+
+
+def w8a8_linear_noalloc(a, a_scale, w, w_scale, bias, y, acc_out=None, stream=None) -> None:
+    """w8a8_linear with the K-split partials in the library's static device scratch."""
+    M, K = a.shape
+    N = w.shape[0]
+    _check(lib().w8a8_linear_noalloc(_p(a), _p(a_scale), M, K, _p(w), _p(w_scale), _p(bias), N, _p(y), _dt(y),
+                                     y.stride(0), _p(acc_out), _stream(stream)), "w8a8_linear_noalloc")
 
 
 def bf16_linear(a, w, bias, y, stream=None) -> None:

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/dit.h"
@@ -117,6 +118,38 @@ EpiParams store_epi(void* y, int64_t ldy, bool y_bf16, const float* bias) {
     return ep;
 }
 
+// ---- device scratch of w8a8_linear_noalloc (for callers that cannot allocate)
+// The K-split partial sums of w8a8_linear_noalloc live in this array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel (in host code it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and is kept in scratch_ptr[].
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+int noalloc_scratch(void** out) {
+    int dev = -1;
+    RUN(hipGetDevice(&dev), "hipGetDevice");
+    CHECK(dev >= 0 && dev < kMaxDevices, DIT_E_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        RUN(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        CHECK(p != nullptr && aligned16(p), DIT_E_HIP, "scratch symbol address invalid");
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return DIT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,9 +203,8 @@ int dit_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int64_t ldu, int
 
 size_t w8a8_linear_workspace_bytes(void) { return (size_t)kSplitPartialBytes; }
 
-int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
-                const float* w_scale, const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy,
-                int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+static int check_w8a8_args(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
+                           const float* w_scale, int64_t N, const void* y, int y_dtype, int64_t ldy) {
     CHECK(y_dtype == DIT_BF16 || y_dtype == DIT_F32, DIT_E_DTYPE, "y_dtype must be bf16 or f32");
     CHECK(M >= 0 && K >= 1 && N >= 1 && ldy >= N, DIT_E_SHAPE, "need M>=0, K>=1, N>=1, ldy>=N");
     CHECK(K % 128 == 0, DIT_E_UNSUPPORTED, "K=%lld must be a multiple of 128", (long long)K);
@@ -181,11 +213,20 @@ int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, con
     CHECK(((M + 127) / 128) * ((N + 127) / 128) < 0x7fffffff, DIT_E_UNSUPPORTED, "too many tiles");
     CHECK(M * K < ((int64_t)1 << 31) && N * K < ((int64_t)1 << 31), DIT_E_UNSUPPORTED,
           "operands must be below 2 GiB");
-    CHECK(workspace == nullptr || workspace_bytes >= w8a8_linear_workspace_bytes(), DIT_E_WORKSPACE,
-          "workspace needs %zu bytes", w8a8_linear_workspace_bytes());
     if (M == 0) return DIT_OK;
     CHECK(a && a_scale && w && w_scale && y, DIT_E_NULL, "a, a_scale, w, w_scale and y must be non-NULL");
     CHECK(aligned16(a) && aligned16(w), DIT_E_ALIGN, "a and w must be 16-byte aligned");
+    return DIT_OK;
+}
+
+int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
+                const float* w_scale, const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy,
+                int32_t* acc_out, void* workspace, size_t workspace_bytes, void* stream) {
+    int s = check_w8a8_args(a, a_scale, M, K, w, w_scale, N, y, y_dtype, ldy);
+    if (s) return s;
+    CHECK(workspace == nullptr || workspace_bytes >= w8a8_linear_workspace_bytes(), DIT_E_WORKSPACE,
+          "workspace needs %zu bytes", w8a8_linear_workspace_bytes());
+    if (M == 0) return DIT_OK;
     CHECK(workspace == nullptr || aligned16(workspace), DIT_E_ALIGN, "workspace must be 16-byte aligned");
     EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
     ep.a_scale = a_scale;
@@ -197,6 +238,26 @@ int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K, con
         ep.split_bytes = kSplitPartialBytes;
     }
     RUN(launch_gemm_i8(a, w, M, N, K, ep, S(stream)), "w8a8_linear");
+    return DIT_OK;
+}
+
+int w8a8_linear_noalloc(const int8_t* a, const float* a_scale, int64_t M, int64_t K, const int8_t* w,
+                        const float* w_scale, const float* bias, int64_t N, void* y, int y_dtype, int64_t ldy,
+                        int32_t* acc_out, void* stream) {
+    int s = check_w8a8_args(a, a_scale, M, K, w, w_scale, N, y, y_dtype, ldy);
+    if (s) return s;
+    if (M == 0) return DIT_OK;
+    void* part = nullptr;
+    s = noalloc_scratch(&part);
+    if (s) return s;
+    EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    ep.a_scale = a_scale;
+    ep.w_scale = w_scale;
+    ep.acc_out = acc_out;
+    ep.ldacc = N;
+    ep.split_partial = (int32_t*)part;
+    ep.split_bytes = (int64_t)kNoAllocScratchBytes;
+    RUN(launch_gemm_i8(a, w, M, N, K, ep, S(stream)), "w8a8_linear_noalloc");
     return DIT_OK;
 }
 

@@ -794,7 +794,9 @@ static int plan_split(int64_t tiles, int nk, const EpiParams& ep, int64_t* full)
     if (r == 0) return 0;
     int S = (int)std::min<int64_t>(C / r, 16);
     S = std::min(S, nk / 8);
-    if (S < 2 || r * S * (int64_t)L_BM * L_BN * 4 > ep.split_bytes) return 0;
+    // a smaller scratch takes fewer K ranges per tile
+    S = (int)std::min<int64_t>(S, ep.split_bytes / (r * (int64_t)L_BM * L_BN * 4));
+    if (S < 2) return 0;
     *full = R * C;
     return S;
 }

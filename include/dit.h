@@ -104,6 +104,22 @@ int w8a8_linear(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
                 size_t workspace_bytes, void* stream);
 
 /*
+ * w8a8_linear for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same linear, the
+ * same arguments without the workspace, bitwise-equal results.  The K-split
+ * partial sums go to the library's own device scratch, a static array of
+ * 32 MiB per GPU (held until the process ends); a launch whose split would
+ * need more takes fewer K ranges.  The scratch is fully written before it is
+ * read, so it needs no clearing; it is shared by every call on one GPU, so
+ * calls that overlap on one GPU (different streams or threads) race.  The
+ * first call on each device looks up the scratch address (no allocation,
+ * library call or memset otherwise).  Errors as w8a8_linear.
+ */
+int w8a8_linear_noalloc(const int8_t* a, const float* a_scale, int64_t M, int64_t K,
+                        const int8_t* w, const float* w_scale, const float* bias, int64_t N,
+                        void* y, int y_dtype, int64_t ldy, int32_t* acc_out, void* stream);
+
+/*
  * Asymmetric per-row int8 quantization ("Qwen-Image-2.1 W8A8 - FlagOS for Mac",
  * Quantization and validation: dynamic asymmetric INT8 activations per token,
  * fp32 scales).  The page gives no formula; reading: the row's range widened to
