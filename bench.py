@@ -18,7 +18,8 @@ also with the int8/fp8 attention.
 Also measured (reported under "gated_recipe_1024px"): one gated-MLP block
 (F 12288) over the same tokens, all-bf16, with the FlagOS page's W8A8 scope
 (Q/K, proj and gate int8 with asymmetric per-token activations), and with all
-six linears stored as MXFP4 (expanded to bf16 per call, bf16 arithmetic).
+six linears stored as MXFP4 (decoded to bf16 in the GEMM's operand staging,
+bf16 arithmetic).
 
 Also measured (reported under "small_blocks"): one block of the 256x256
 generation in bf16 ([64 text | 256 image] tokens) and one of the 512x512

@@ -316,8 +316,14 @@ int mxfp4_linear(const void* a, int64_t M, int64_t K, int64_t lda, const uint8_t
     CHECK(aligned16(a) && aligned16(codes) && aligned16(workspace), DIT_E_ALIGN,
           "a, codes and workspace must be 16-byte aligned");
     hipStream_t st = S(stream);
-    RUN(launch_mxfp4_expand(codes, scales, N, K, workspace, st), "mxfp4_expand");
     EpiParams ep = store_epi(y, ldy, y_dtype == DIT_BF16, bias);
+    if (gemm_bf16_direct_mxfp4(M, N, K, lda, false) && N * (K / 2) < ((int64_t)1 << 31)) {
+        // the large-tile GEMM decodes the codes in its operand staging
+        ep.w_mx_scale = scales;
+        RUN(launch_gemm_bf16(a, lda, codes, M, N, K, ep, st), "mxfp4_linear");
+        return DIT_OK;
+    }
+    RUN(launch_mxfp4_expand(codes, scales, N, K, workspace, st), "mxfp4_expand");
     RUN(launch_gemm_bf16(a, lda, workspace, M, N, K, ep, st), "mxfp4_linear");
     return DIT_OK;
 }
@@ -912,6 +918,11 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
         e.split_partial = split_partial;
         e.split_bytes = kSplitPartialBytes;
         if (L.mx_scale) {
+            if (gemm_bf16_direct_mxfp4(T, N, K, K, true)) {
+                // decoded in the GEMM's operand staging
+                e.w_mx_scale = L.mx_scale;
+                return launch_gemm_bf16(A, K, L.w, T, N, K, e, st);
+            }
             const hipError_t x = launch_mxfp4_expand((const uint8_t*)L.w, L.mx_scale, N, K, ws + p.wx, st);
             if (x != hipSuccess) return x;
             return launch_gemm_bf16(A, K, ws + p.wx, T, N, K, e, st);

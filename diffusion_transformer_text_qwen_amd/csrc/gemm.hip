@@ -399,7 +399,12 @@ __device__ __forceinline__ void tile_origin(int tau, int tiles_m, int tiles_n, i
 // WN: waves along N (4: 2 x 4 waves of 128 x 64; 2: 4 x 2 waves of 64 x 128,
 // so that one wave holds whole 128-column heads for the fused QKV epilogue).
 // Either way a wave reads 12 fragments per step and issues 32 MFMAs.
-template <bool I8, int EV, int WN>
+// W4 (bf16 A only): W holds MXFP4 codes [N, K/2] (E2M1, element 2i in the low
+// nibble of byte i) with E8M0 scales ep.w_mx_scale [N, K/32]; each stage's W
+// tile is decoded to bf16 in registers (hardware fp4 -> bf16 conversion with
+// the fp32 scale) and written to the LDS slot, so 4.25 bits per weight come
+// from memory.  Thread t decodes 32 values: row t/2, K half t%2 of the stage.
+template <bool I8, int EV, int WN, bool W4 = false>
 __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_t lda_b,
                                            const uint8_t* __restrict__ W, int64_t M, int64_t N, int64_t Kb,
                                            const EpiParams& ep, uint8_t* lds, int64_t m0, int64_t n0, int ks0,
@@ -407,6 +412,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     const int tid = threadIdx.x;
     const int lane = tid % kWave, wave = tid / kWave;
     static_assert(WN == 4 || WN == 2, "wave grid");
+    static_assert(!(W4 && I8), "MXFP4 weights go with bf16 activations");
     static_assert(EV != EV_QKV || WN == 2, "the fused QKV epilogue needs whole heads per wave");
     constexpr int WTM = L_BM / (8 / WN), WTN = L_BN / WN;   // wave tile
     constexpr int MF = WTM / 16, NF = WTN / 16;             // 16 x 16 accumulator tiles
@@ -422,13 +428,30 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     // of a stage is the scalar soffset.
     typedef __attribute__((address_space(3))) void* lds_ptr_t;
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(M * lda_b), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rs_w = __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(N * Kb), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs_w =
+        __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(W4 ? N * (Kb / 4) : N * Kb), 0x00020000);
     int aoff[4], boff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int p = (wave * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
         aoff[i] = (int)(min(m0 + r, M - 1) * lda_b) + c * 16;
         boff[i] = (int)(min(n0 + r, N - 1) * Kb) + c * 16;
+    }
+    // MXFP4 W: code and scale offsets of this thread's row and K half; LDS
+    // byte offset of its row in the W part of a slot
+    const __amdgpu_buffer_rsrc_t rs_s4 = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ep.w_mx_scale, 0, W4 ? (int)(N * (Kb / 64)) : 0, 0x00020000);
+    int w4_off = 0, s4_off = 0, w4_lds = 0, w4_sw = 0;
+    v4i w4_codes = {0, 0, 0, 0};
+    uint32_t w4_scale = 0;
+    if constexpr (W4) {
+        const int row = tid >> 1, half = tid & 1;
+        const int64_t gr = min(n0 + row, N - 1);
+        w4_off = (int)(gr * (Kb / 4)) + half * 16;
+        s4_off = (int)(gr * (Kb / 64)) + half;
+        w4_lds = L_TILE_BYTES + row * L_SK;
+        w4_sw = (row & 7) | (half << 5);   // chunk c = 4 half + j sits at slot c ^ (row & 7)
+        (void)boff;
     }
     const int wbase = __builtin_amdgcn_readfirstlane(wave * 4 * 1024);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
@@ -448,8 +471,32 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
         uint8_t* sl = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES + wbase;                       \
         _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(sl + i * 1024), 16, aoff[i], kb0, 0, 0); \
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + L_TILE_BYTES + i * 1024), 16, boff[i], \
-                                                     kb0, 0, 0);                              \
+            if constexpr (!W4)                                                                \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + L_TILE_BYTES + i * 1024), 16, \
+                                                         boff[i], kb0, 0, 0);                 \
+        }                                                                                     \
+    } while (0)
+// MXFP4 W: codes and scale of a stage into registers (issued one stage before
+// they are decoded), then decoded into the stage's slot
+#define W4_LOAD(stage)                                                                        \
+    do {                                                                                      \
+        const int kb0 = ks0 * L_BK + (stage) * L_SK;                                          \
+        w4_codes = (v4i)__builtin_amdgcn_raw_buffer_load_b128(rs_w, w4_off, kb0 / 4, 0);       \
+        w4_scale = __builtin_amdgcn_raw_buffer_load_b8(rs_s4, s4_off, kb0 / 64, 0);            \
+    } while (0)
+#define W4_STORE(stage)                                                                       \
+    do {                                                                                      \
+        uint8_t* sl = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES + w4_lds;                      \
+        const float sc = w4_scale == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)w4_scale - 127); \
+        _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
+            const uint32_t word = (uint32_t)w4_codes[j];                                      \
+            v4i o;                                                                            \
+            o[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 0)); \
+            o[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 1)); \
+            o[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 2)); \
+            o[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sc, 3)); \
+            const int chunk = ((w4_sw >> 5) * 4 + j) ^ (w4_sw & 7);                          \
+            *reinterpret_cast<v4i*>(sl + (chunk << 4)) = o;                                   \
         }                                                                                     \
     } while (0)
 // fragments of step half H of the stage in slot (stage % 2)
@@ -494,12 +541,19 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 // is done, so step 2s+1 may refill slot s and read slot s+1.  Nothing needs a
 // barrier after step 2s+1: the next refill of slot s+1 waits for the barrier
 // after step 2s+2.
-#define LG_PAIR(s, LOADS)                                       \
+// With MXFP4 W the barrier also covers the codes of stage s+2 (loaded one stage
+// earlier); they are decoded into the freed slot, and the codes of stage s+3
+// are loaded (W4_NEXT).
+#define LG_PAIR(s, LOADS, W4_NEXT)                              \
     do {                                                        \
         LG_FRAGS(s, 1, fa1, fb1);                               \
         LG_MFMA(fa0, fb0);                                      \
         LG_SCHEDULE(false);                                     \
         LG_BARRIER(0);                                          \
+        if constexpr (W4) {                                     \
+            if (LOADS) W4_STORE((s) + 2);                       \
+            if (W4_NEXT) W4_LOAD((s) + 3);                      \
+        }                                                       \
         if (LOADS) LG_DMA((s) + 2);                             \
         LG_FRAGS((s) + 1, 0, fa0, fb0);                         \
         LG_MFMA(fa1, fb1);                                      \
@@ -539,12 +593,35 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     }
 
     // prologue: stages 0 and 1 in flight, wait for 0, fragments of step 0
-    LG_DMA(0);
-    if (nst > 1) {
-        LG_DMA(1);
-        LG_BARRIER(8);
+    if constexpr (W4) {
+        // codes of stages 0 and 1 decoded before the first barrier, those of
+        // stage 2 in flight (two loads per thread and stage)
+        W4_LOAD(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        W4_STORE(0);
+        if (nst > 1) {
+            W4_LOAD(1);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            W4_STORE(1);
+        }
+        LG_DMA(0);
+        if (nst > 1) LG_DMA(1);
+        if (nst > 2) {
+            W4_LOAD(2);
+            LG_BARRIER(6);
+        } else if (nst > 1) {
+            LG_BARRIER(4);
+        } else {
+            LG_BARRIER(0);
+        }
     } else {
-        LG_BARRIER(0);
+        LG_DMA(0);
+        if (nst > 1) {
+            LG_DMA(1);
+            LG_BARRIER(8);
+        } else {
+            LG_BARRIER(0);
+        }
     }
     frag_t fa0[MF], fb0[NF], fa1[MF], fb1[NF];
     LG_FRAGS(0, 0, fa0, fb0);
@@ -552,14 +629,24 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     // Stages that load stage s+2, then the last two without loads.  The step
     // after the last reads fragments of a slot nobody uses (harmless).
     int s = 0;
-    for (; s + 2 < nst; ++s) LG_PAIR(s, true);
-    for (; s < nst; ++s) LG_PAIR(s, false);
+    if constexpr (W4) {
+        for (; s + 3 < nst; ++s) LG_PAIR(s, true, true);
+        if (s + 2 < nst) {
+            LG_PAIR(s, true, false);
+            ++s;
+        }
+    } else {
+        for (; s + 2 < nst; ++s) LG_PAIR(s, true, false);
+    }
+    for (; s < nst; ++s) LG_PAIR(s, false, false);
     // every load has landed (the last barrier waited for all); the epilogue
     // reuses LDS once every wave's fragment reads are done
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 #undef LG_DMA
+#undef W4_LOAD
+#undef W4_STORE
 #undef LG_FRAGS
 #undef LG_BARRIER
 #undef LG_MFMA
@@ -696,7 +783,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     asm volatile("" ::: "memory");
 }
 
-template <bool I8, int EV, int WN>
+template <bool I8, int EV, int WN, bool W4 = false>
 __global__ void __launch_bounds__(L_THREADS, 1)
 gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
                   int64_t M, int64_t N, int64_t Kb, EpiParams ep, LargePlan lp) {
@@ -734,7 +821,7 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         }
         int64_t m0, n0;
         tile_origin(tau, tiles_m, tiles_n, m0, n0);
-        large_tile<I8, EV, WN>(A, lda_b, W, M, N, Kb, ep, lds, m0, n0, ks0, nk, part);
+        large_tile<I8, EV, WN, W4>(A, lda_b, W, M, N, Kb, ep, lds, m0, n0, ks0, nk, part);
     }
 }
 
@@ -868,17 +955,24 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     }
 }
 
-template <bool I8, int EV>
+// The large kernel addresses each operand with 32-bit buffer offsets.
+static bool takes_large(int64_t M, int64_t N, int64_t lda_b, int64_t Kb, bool can_split) {
+    return use_large(M, N, (int)(Kb / L_BK), can_split) && lda_b % 16 == 0 && Kb % L_SK == 0 &&
+           M * lda_b < ((int64_t)1 << 31) && N * Kb < ((int64_t)1 << 31);
+}
+
+bool gemm_bf16_direct_mxfp4(int64_t M, int64_t N, int64_t K, int64_t lda, bool can_split) {
+    return takes_large(M, N, lda * 2, K * 2, can_split);
+}
+
+template <bool I8, int EV, bool W4 = false>
 static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                         const EpiParams& ep, hipStream_t st) {
     constexpr int kWN = EV == EV_QKV ? 2 : 4;
-    // the large kernel addresses each operand with 32-bit buffer offsets
-    if (use_large(M, N, (int)(Kb / L_BK), ep.split_partial != nullptr) && lda_b % 16 == 0 &&
-        Kb % L_SK == 0 && M * lda_b < ((int64_t)1 << 31) &&
-        N * Kb < ((int64_t)1 << 31)) {
+    if (W4 || takes_large(M, N, lda_b, Kb, ep.split_partial != nullptr)) {
         static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
         if (!lds_set) {
-            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN>,
+            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN, W4>,
                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
             lds_set = true;
         }
@@ -890,17 +984,17 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
         if (S && Kb / L_BK > 64) {
             // long K loops: whole tiles, then the K ranges of the split tiles
             if (full > 0)
-                gemm_large_kernel<I8, EV, kWN><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
+                gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
                     a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
-            gemm_large_kernel<I8, EV, kWN><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
+            gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
                 a, lda_b, w, M, N, Kb, ep, LargePlan{0, (int32_t)full, r, S});
         } else {
             // persistent: at most one workgroup per compute unit, and one for
             // each split range (r * S <= C)
             const int64_t G = std::min<int64_t>(C, std::max<int64_t>(full > 0 ? tiles : 0, (int64_t)r * S));
-            gemm_large_kernel<I8, EV, kWN><<<(unsigned)(G > 0 ? G : std::min<int64_t>(C, tiles)), L_THREADS,
-                                             L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
-                                                          LargePlan{(int32_t)full, (int32_t)full, r, S});
+            gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)(G > 0 ? G : std::min<int64_t>(C, tiles)), L_THREADS,
+                                                 L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
+                                                              LargePlan{(int32_t)full, (int32_t)full, r, S});
         }
         if (S) split_reduce_kernel<I8, EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
     }
@@ -919,6 +1013,17 @@ static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64
 template <bool I8>
 static void launch_mfma_any(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                             const EpiParams& ep, hipStream_t st) {
+    if constexpr (!I8) {
+        if (ep.w_mx_scale != nullptr) {
+            switch (variant(ep)) {
+                case EV_GELU: launch_mfma<false, EV_GELU, true>(a, lda_b, w, M, N, Kb, ep, st); break;
+                case EV_QKV: launch_mfma<false, EV_QKV, true>(a, lda_b, w, M, N, Kb, ep, st); break;
+                case EV_RESID: launch_mfma<false, EV_RESID, true>(a, lda_b, w, M, N, Kb, ep, st); break;
+                default: launch_mfma<false, EV_STORE, true>(a, lda_b, w, M, N, Kb, ep, st); break;
+            }
+            return;
+        }
+    }
     switch (variant(ep)) {
         case EV_STORE: launch_mfma<I8, EV_STORE>(a, lda_b, w, M, N, Kb, ep, st); break;
         case EV_STORE_ACC: launch_mfma<I8, EV_STORE_ACC>(a, lda_b, w, M, N, Kb, ep, st); break;

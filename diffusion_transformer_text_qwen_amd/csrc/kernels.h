@@ -57,6 +57,10 @@ struct EpiParams {
     // tensor (the gated MLP's proj output).
     const void* gmul;
     int64_t ldgm;
+    // bf16 GEMM only (NULL = bf16 weights): W holds MXFP4 codes [N, K/2] and
+    // these are its E8M0 scales [N, K/32], decoded in the operand staging.
+    // Only shapes that gemm_bf16_direct_mxfp4 accepts.
+    const uint8_t* w_mx_scale;
 };
 
 // Bytes of split scratch the int8 GEMM may use for any shape: at most C tiles x
@@ -67,6 +71,9 @@ hipError_t launch_gemm_i8(const int8_t* a, const int8_t* w, int64_t M, int64_t N
                           const EpiParams& ep, hipStream_t st);
 hipError_t launch_gemm_bf16(const void* a, int64_t lda, const void* w, int64_t M, int64_t N,
                             int64_t K, const EpiParams& ep, hipStream_t st);
+// Whether the bf16 GEMM of this shape runs on the large-tile kernel, which can
+// decode MXFP4 weights in its operand staging (ep.w_mx_scale).
+bool gemm_bf16_direct_mxfp4(int64_t M, int64_t N, int64_t K, int64_t lda, bool can_split);
 hipError_t launch_gemm_f32(const float* a, int64_t lda, const float* w, int64_t M, int64_t N,
                            int64_t K, const EpiParams& ep, hipStream_t st);
 

@@ -400,9 +400,13 @@ int dit_stack_forward(const dit_block_config* cfg, const dit_block_weights* weig
  * range.
  * dit_mxfp4_expand: codes [N, K/2] uint8, scales [N, K/32] uint8 -> w_bf16 [N, K]
  * (row stride K).  K % 32 == 0; codes and w_bf16 16-byte aligned.
- * mxfp4_linear: y = a w^T + bias with w given as MXFP4 (expanded into the
- * workspace, mxfp4_linear_workspace_bytes(N, K) bytes, then the bf16 linear);
- * a [M, K] bf16 (row stride lda), y bf16|f32 (row stride ldy).  K % 64 == 0.
+ * mxfp4_linear: y = a w^T + bias with w given as MXFP4; a [M, K] bf16 (row
+ * stride lda), y bf16|f32 (row stride ldy).  Shapes that fill the GPU with
+ * 256 x 256 tiles decode the codes to bf16 in the GEMM's operand staging (the
+ * weights cross HBM at 4.25 bits per value; the workspace is not touched);
+ * smaller shapes expand the weights into the workspace,
+ * mxfp4_linear_workspace_bytes(N, K) bytes, then run the bf16 linear.  Both
+ * give bitwise the bf16 linear on the decoded weights.  K % 64 == 0.
  */
 int dit_mxfp4_expand(const uint8_t* codes, const uint8_t* scales, int64_t N, int64_t K, void* w_bf16,
                      void* stream);
@@ -419,8 +423,10 @@ int mxfp4_linear(const void* a, int64_t M, int64_t K, int64_t lda, const uint8_t
  * linears run W8A8).  s != NULL: w holds int8 codes [N, K] (symmetric per
  * output channel, scales s [N]) and wsum [N] their row sums (dit_int8_colsum);
  * the activation is quantized asymmetrically per token (dit_quantize_rows_asym).
- * mx_scale != NULL: MXFP4 weights (see dit_mxfp4_expand), expanded to bf16 in
- * the workspace for the call.  Otherwise w is bf16 [N, K] and wsum is ignored.
+ * mx_scale != NULL: MXFP4 weights (see dit_mxfp4_expand), decoded in the
+ * GEMM's operand staging (or, for shapes too small for the large-tile GEMM,
+ * expanded to bf16 in the workspace for the call).  Otherwise w is bf16 [N, K]
+ * and wsum is ignored.
  * b: fp32 bias [N] or NULL.
  */
 typedef struct {

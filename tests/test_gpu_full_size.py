@@ -82,14 +82,21 @@ def test_velocity_forward_1024px_four_blocks():
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("scope", ["page", "all"])
+@pytest.mark.parametrize("scope", ["page", "all", "mxfp4"])
 def test_gated_block_1024px_full_width(scope):
+    """scope: the page's W8A8 linears, every linear W8A8, or every linear
+    MXFP4 (decoded in the GEMM's operand staging at this size)."""
     w = ditsynth.custom("gated1024", 4096, 32, 12288, 256, [(64, 64)], "bf16", 62)
     T = w.T
     say("gated block 1024px F=12288", scope, T)
     arrays = ditsynth.gated_block_weights(w, 0)
     inp = ditsynth.block_inputs(w)
-    int8 = ("qk", "proj", "gate") if scope == "page" else dq.GATED_LINEARS
+    int8 = {"page": ("qk", "proj", "gate"), "all": dq.GATED_LINEARS, "mxfp4": ()}[scope]
+    mx = None
+    if scope == "mxfp4":
+        D, F = w.D, w.F
+        shapes = {"qk": (2 * D, D), "v": (D, D), "o": (D, D), "proj": (F, D), "gate": (F, D), "down": (D, F)}
+        mx = {n: ditsynth.mxfp4_weights(*shp, seed=80 + i) for i, (n, shp) in enumerate(shapes.items())}
     cfg = dq.block_config("bf16", w.D, w.H, w.F)
     cos = torch.empty((T, 64), dtype=torch.float32, device=DEV)
     sin = torch.empty((T, 64), dtype=torch.float32, device=DEV)
@@ -98,7 +105,7 @@ def test_gated_block_1024px_full_width(scope):
     k = torch.zeros((T, w.H, 128), dtype=torch.bfloat16, device=DEV)
     v = torch.zeros_like(k)
     ws = torch.empty(dq.gated_workspace_bytes(cfg, T, T), dtype=torch.uint8, device=DEV)
-    gw = dq.GatedBlockWeights(arrays, int8)
+    gw = dq.GatedBlockWeights(arrays, int8, mx=mx)
     dq.block_forward_gated(cfg, gw, x, dev(inp["mod"]), inp["mod_of_seg"], cos, sin, w.seg_len, k, v, ws)
     torch.cuda.synchronize()
     got = host(x)
@@ -106,7 +113,8 @@ def test_gated_block_1024px_full_width(scope):
     torch.cuda.empty_cache()
     c, s = oracle.rope_tables(oracle.rope_positions(w.text, w.images))
     ref = oracle.block_forward_gated(inp["x"], inp["mod"], inp["mod_of_seg"], inp["seg_len"], c, s, arrays,
-                                     int8=tuple("w_" + n for n in int8))["x_out"]
+                                     int8=tuple("w_" + n for n in int8),
+                                     mx={"w_" + n: cs for n, cs in mx.items()} if mx else None)["x_out"]
     x0 = inp["x"].astype(np.float64)
     e_out, e_delta = rel_l2(got, ref), rel_l2(got - x0, ref - x0)
     say(f"  gated {scope}: rel_l2 out {e_out:.3e} delta {e_delta:.3e}")

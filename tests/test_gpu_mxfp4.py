@@ -51,6 +51,31 @@ def test_mxfp4_linear(M, N, K):
     assert np.all(np.abs(host(yf)[rows] - ref) <= acc_bound + 1e-30)
 
 
+@pytest.mark.parametrize("M,N,K", [(4352, 4096, 4096), (4429, 4144, 2048), (1024, 12288, 4096)])
+def test_mxfp4_linear_decoded_in_staging_equals_expanded(M, N, K):
+    """Shapes on the large-tile GEMM decode the MXFP4 codes in its operand
+    staging: bitwise the bf16 linear on the expanded weights (same tiles, same
+    MFMA order), including ragged M and N."""
+    say("mxfp4 direct", M, N, K)
+    rng = np.random.default_rng(M + N + K)
+    a = ditsynth.to_bf16_grid(rng.standard_normal((M, K)).astype(np.float32))
+    codes, scales = ditsynth.mxfp4_weights(N, K, seed=K)
+    bias = ditsynth.to_bf16_grid((rng.standard_normal(N) * 0.02).astype(np.float32))
+    ad, cd, sd, bd = dev(a, torch.bfloat16), dev(codes, torch.uint8), dev(scales, torch.uint8), dev(bias)
+    ws = torch.full((dq.lib().mxfp4_linear_workspace_bytes(N, K),), 0x7F, dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    dq.mxfp4_linear(ad, cd, sd, bd, y, ws)
+    w_exp = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    dq.mxfp4_expand(cd, sd, w_exp)
+    y2 = torch.empty_like(y)
+    dq.bf16_linear(ad, w_exp, bd, y2)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    # the workspace (the expansion target of small shapes) is not touched
+    assert bool((ws == 0x7F).all())
+    np.testing.assert_array_equal(host(w_exp)[::97], oracle.mxfp4_decode(codes[::97], scales[::97]))
+
+
 @pytest.mark.parametrize("attn_quant", [False, True])
 def test_gated_block_with_mxfp4_linears(attn_quant):
     """All six linears MXFP4 (the page's checkpoint quantizes every main matrix)."""
