@@ -39,10 +39,14 @@ events the library records around each launch during K more timed steps
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-edit]
   python bench.py --copy-probe MIB   # plain bf16 copy of MIB MiB, for HBM counter calibration
 
-roofline.traffic: HBM bytes per int8 GEMM launch from rocprofv3 FETCH_SIZE and
+roofline.traffic: bytes per int8 GEMM launch site from rocprofv3 FETCH_SIZE and
 WRITE_SIZE passes over this script, each divided by what the same counter reads
-per byte of the --copy-probe copy (profiles/gemm_w8a8_1024px_traffic.json); it
-is null when gemm.hip no longer matches the hash recorded with the counters.
+per byte of the --copy-probe copy (profiles/gemm_w8a8_1024px_traffic.json).
+These counters count L2 misses to the data fabric (part of which the memory-side
+cache serves), so the figure bounds HBM bytes from above.  It is null when
+gemm.hip no longer matches the hash recorded with the counters.  The adaLN and
+quantization kernels' entries in "kernels" carry the same counters' bytes
+(profiles/hbm_kernels_1024px_traffic.json) next to their algorithmic bytes.
 """
 from __future__ import annotations
 
@@ -120,6 +124,25 @@ def gemm_traffic():
     return int(fetch + write)
 
 
+def hbm_kernel_traffic():
+    """Counter-derived bytes (read + written) per dispatch of the adaLN and row
+    quantization kernels ({site: bytes}), or {} if stale/absent."""
+    path = os.path.join(ROOT, "profiles", "hbm_kernels_1024px_traffic.json")
+    src = os.path.join(ROOT, "diffusion_transformer_text_qwen_amd", "csrc", "elementwise.hip")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+        with open(src, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return {}
+    if t.get("elementwise_source_sha256") != sha:
+        return {}
+    k = t["kernels"]
+    by = {name: v["bytes_read"] + v["bytes_written"] for name, v in k.items()}
+    return {"adaln1": by["adaln"], "adaln2": by["adaln"], "quant_o": by["quant_o"], "quant_g": by["quant_g"]}
+
+
 def copy_probe(mib, dq, torch):
     """dit_cast bf16 -> bf16 over mib MiB: reads and writes exactly 2n bytes."""
     n = mib * (1 << 20) // 2
@@ -130,6 +153,25 @@ def copy_probe(mib, dq, torch):
     torch.cuda.synchronize()
     print(json.dumps({"copy_probe": {"dispatches": 5, "bytes_read_per_dispatch": 2 * n,
                                      "bytes_written_per_dispatch": 2 * n}}), flush=True)
+
+
+def counter_summary(root):
+    """Per kernel: dispatch count and the mean per dispatch of every counter in
+    the rocprofv3 --pmc csv output under root (one JSON line per kernel)."""
+    import csv
+    import glob
+    agg, ids = {}, {}
+    for f in glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                k = r["Kernel_Name"]
+                agg.setdefault(k, {}).setdefault(r["Counter_Name"], 0.0)
+                agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+                ids.setdefault(k, set()).add(r["Dispatch_Id"])
+    for k in sorted(agg, key=lambda k: -len(ids[k])):
+        n = len(ids[k])
+        print(json.dumps({"kernel": k, "dispatches": n,
+                          "mean": {c: v / n for c, v in sorted(agg[k].items())}}))
 
 
 def site_report(prof, per_block_ops, n_blocks_timed, peak, unit):
@@ -477,9 +519,14 @@ def main():
     ap.add_argument("--no-edit", action="store_true")
     ap.add_argument("--edit-reps", type=int, default=5)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB")
+    ap.add_argument("--counter-summary", default="", metavar="DIR",
+                    help="print per-kernel means of the rocprofv3 --pmc csv files under DIR and exit")
     ap.add_argument("--loop-steps", type=int, default=40,
                     help="steps of the timed denoise loop after the step benchmark (0: skip)")
     args = ap.parse_args()
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               f"(the multi-GPU design is described, not built).", file=sys.stderr)
@@ -510,6 +557,14 @@ def main():
     kernels.update(site_report(prof, g_ops, n_timed, PEAK_INT8_TOPS, "TOPS"))
     kernels.update(site_report(prof, {"attention": att_flops}, n_timed, PEAK_BF16_TFLOPS, "TFLOPS"))
     kernels.update(site_report(prof, hbm_bytes(T, D, F), n_timed, PEAK_HBM_GBS, "GB/s"))
+    # the same kernels' bytes from the FETCH_SIZE / WRITE_SIZE counters (taken
+    # with the current elementwise source), at this run's launch times
+    for site, nbytes in hbm_kernel_traffic().items():
+        if site in kernels:
+            rate = nbytes / (kernels[site]["avg_us"] * 1e-6) / 1e9
+            kernels[site]["counter_bytes"] = nbytes
+            kernels[site]["counter_GB/s"] = round(rate, 1)
+            kernels[site]["counter_frac_peak"] = round(rate / PEAK_HBM_GBS, 4)
     block_ms = sum(p["ms"] for p in prof.values()) / n_timed
     line = {
         "metric": METRIC,
@@ -531,6 +586,9 @@ def main():
                    "heads": w.H, "mlp": F, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                      "frac": round(achieved / PEAK_INT8_TOPS, 4), "traffic": gemm_traffic(),
+                     "traffic_note": "FETCH_SIZE + WRITE_SIZE per launch site, calibrated by a plain copy: bytes "
+                                     "that miss the XCD L2s (fabric bytes; the memory-side cache serves part of "
+                                     "them), an upper bound on HBM bytes",
                      "kernel": "gemm_large_kernel<int8> (+ K-split tail and its reduce): the four W8A8 "
                                "linears of a block, one launch site each",
                      "algorithmic_ops_per_launch": int(avg_launch_ops),
