@@ -653,6 +653,22 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 #undef LG_SCHEDULE
 #undef LG_PAIR
 
+    if (part != nullptr) {
+        // K-split partial sums go straight from the accumulators, in fragment
+        // order: 16-byte piece ((((wm MF + i) WN + wn) NF + j) 64 + lane) holds
+        // acc[i][j], so each store of a wave is 1 KB contiguous and the 16 KB
+        // of tile rows [16 b, 16 b + 16) are contiguous (WN NF = 16).  Row
+        // blocks at or past M are not stored (their reduce returns first).
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            if (m0 + wm * WTM + i * 16 >= M) break;
+#pragma unroll
+            for (int j = 0; j < NF; ++j)
+                reinterpret_cast<acc_t*>(part)[((((wm * MF + i) * WN + wn) * NF + j) << 6) + lane] = acc[i][j];
+        }
+        return;
+    }
+
     // Epilogue: for each 16-row slab i, every wave parks its 16 x WTN slab of
     // accumulators in its own LDS region, then each lane finishes 16
     // consecutive columns of one row (LPR lanes per row, RPP rows per pass).
@@ -663,7 +679,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     const int64_t n = n0 + wn * WTN + ec;
     QkvAux aux;
     if constexpr (EV == EV_QKV) {
-        if (part == nullptr) qkv_gain16(ep, n, aux);
+        qkv_gain16(ep, n, aux);
     }
     // Per-lane column constants (weight scales, bias) and the row scales of
     // every slab are loaded once, before the first slab, so that no slab
@@ -671,13 +687,13 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     constexpr int NPASS = 16 / RPP;
     float colw[16], colb[16], rows_sa[MF][NPASS];
     {
-        const bool cb = part == nullptr && n < N && ep.bias != nullptr;
+        const bool cb = n < N && ep.bias != nullptr;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const v4f b4 = cb ? *reinterpret_cast<const v4f*>(ep.bias + n + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
             v4f w4 = {1.f, 1.f, 1.f, 1.f};
             if constexpr (I8) {
-                if (part == nullptr && n < N) w4 = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
+                if (n < N) w4 = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -692,7 +708,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 #pragma unroll
             for (int pass = 0; pass < NPASS; ++pass) {
                 const int64_t m = m0 + wm * WTM + i * 16 + pass * RPP + er0;
-                rows_sa[i][pass] = (part == nullptr && m < M) ? ep.a_scale[m] : 0.0f;
+                rows_sa[i][pass] = m < M ? ep.a_scale[m] : 0.0f;
             }
     }
 #pragma unroll
@@ -714,15 +730,6 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
         for (int pass = 0; pass < 16 / RPP; ++pass) {
             const int er = pass * RPP + er0;
             const int64_t m = m0 + wm * WTM + i * 16 + er;
-            if (part != nullptr) {
-                // partial sums of this K range (int32, or fp32 bits), row-major 256 x 256
-                int32_t* pp = part + (wm * WTM + i * 16 + er) * L_BN + wn * WTN + ec;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<v4i*>(pp + 4 * q) = *reinterpret_cast<const v4i*>(
-                        reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
-                continue;
-            }
             float v[16];
             int32_t ai[16];
             const bool ok = m < M && n < N;
@@ -809,7 +816,13 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
         int32_t* part = nullptr;
         const int jw = (chunk && j > cj) ? j - 1 : j;            // whole-tile round
         if (j == cj) {
-            const int t = b / lp.S, k = b % lp.S;
+            // split job J of workgroup b: XCD x = b % 8 takes the contiguous
+            // job range [x q + min(x, rem), ...) (q = rS / 8, rem = rS % 8), i.e.
+            // all K ranges of neighbouring tiles, so their A and W slices are
+            // fetched into one L2 and shared there
+            const int rS = lp.r * lp.S, x = b % 8, q = rS / 8, rem = rS % 8;
+            const int J = x * q + min(x, rem) + b / 8;
+            const int t = J / lp.S, k = J % lp.S;
             // whole 128-byte stages
             ks0 = 2 * (int)((int64_t)k * (nk_all / 2) / lp.S);
             nk = 2 * (int)((int64_t)(k + 1) * (nk_all / 2) / lp.S) - ks0;
@@ -889,21 +902,44 @@ static int plan_split(int64_t tiles, int nk, const EpiParams& ep, int64_t* full)
 }
 
 // Sum of the S partial tiles of each split tile, then the epilogue.  One
-// workgroup per 16 rows of a tile; thread t owns 16 consecutive columns.
-// int8: int32 partials (exact in any order), then the zero-point correction
-// and the scales; bf16: fp32 partials added in K order.
+// workgroup per 16 rows of a tile: it adds the 16 KB fragment-order block of
+// those rows from each partial (1024 coalesced 16-byte pieces; piece p of the
+// block holds rows 4 ((p % 64) / 16) + e, e < 4, of column 16 (p / 64) + p % 16),
+// transposes the sums through LDS, and thread t finishes 16 consecutive columns
+// of row t / 16.  int8: int32 partials (exact in any order), then the
+// zero-point correction and the scales; bf16: fp32 partials added in K order.
 template <bool I8, int EV>
 __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N, EpiParams ep, int32_t tau0,
                                                            int32_t S) {
+    constexpr int RS = L_BN + 4;   // LDS row stride (words): the 4 rows of a piece hit distinct banks
+    typedef typename std::conditional<I8, int32_t, float>::type elt_t;
+    typedef typename std::conditional<I8, v4i, v4f>::type part_t;
+    __shared__ __attribute__((aligned(16))) elt_t red[16 * RS];
     const int tiles_m = (int)((M + L_BM - 1) / L_BM);
     const int tiles_n = (int)((N + L_BN - 1) / L_BN);
     const int local = blockIdx.x / 16, rb = blockIdx.x % 16;
     int64_t tm0, tn0;
     tile_origin(tau0 + local, tiles_m, tiles_n, tm0, tn0);
-    const int row = rb * 16 + threadIdx.x / 16, col = (threadIdx.x % 16) * 16;
+    if (tm0 + rb * 16 >= M) return;   // row block not stored (whole workgroup)
+    const int t = threadIdx.x;
+    const int32_t* blk = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + rb * 16 * L_BN;
+    part_t sum4[4] = {};
+    for (int s2 = 0; s2 < S; ++s2)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            sum4[u] += reinterpret_cast<const part_t*>(blk + (int64_t)s2 * (L_BM * L_BN))[t + 256 * u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int pc = t + 256 * u, ln = pc & 63;
+        const int col = (pc >> 6) * 16 + (ln & 15), row = (ln >> 4) * 4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[(row + e) * RS + col] = sum4[u][e];
+    }
+    __syncthreads();
+    const int row = rb * 16 + t / 16, col = (t % 16) * 16;
     const int64_t m = tm0 + row, n = tn0 + col;
     if (m >= M || n >= N) return;
-    const int32_t* part = ep.split_partial + (int64_t)local * S * (L_BM * L_BN) + row * L_BN + col;
+    const elt_t* lr = red + (t / 16) * RS + col;
     QkvAux aux;
     if constexpr (EV == EV_QKV) {
         qkv_gain16(ep, n, aux);
@@ -912,11 +948,9 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
     float v[16];
     int32_t ai[16] = {};
     if constexpr (I8) {
-        v4i sum[4] = {};
-        for (int s2 = 0; s2 < S; ++s2)
+        v4i sum[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                sum[q] += *reinterpret_cast<const v4i*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+        for (int q = 0; q < 4; ++q) sum[q] = *reinterpret_cast<const v4i*>(lr + 4 * q);
         if (ep.a_zero) {
             const int za = ep.a_zero[m];
 #pragma unroll
@@ -933,15 +967,12 @@ __global__ void __launch_bounds__(256) split_reduce_kernel(int64_t M, int64_t N,
             }
         }
     } else {
-        v4f sum[4] = {};
-        for (int s2 = 0; s2 < S; ++s2)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                sum[q] += *reinterpret_cast<const v4f*>(part + (int64_t)s2 * (L_BM * L_BN) + 4 * q);
+        for (int q = 0; q < 4; ++q) {
+            const v4f f = *reinterpret_cast<const v4f*>(lr + 4 * q);
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[4 * q + e] = sum[q][e];
+            for (int e = 0; e < 4; ++e) v[4 * q + e] = f[e];
+        }
     }
     if constexpr (EV == EV_QKV) {
         // 16 threads per row; a head's 128 columns are 8 neighbouring lanes
