@@ -19,23 +19,48 @@ def test_counter_summary_means_per_kernel(tmp_path, capsys):
     assert out[1] == {"kernel": "b", "dispatches": 1, "mean": {"FETCH_SIZE": 7.0}}
 
 
-def test_counter_traffic_tracks_the_sources(tmp_path, monkeypatch):
-    """The committed counter files match the committed sources; a copy of the
-    tree whose source differs reports no traffic."""
-    assert bench.gemm_traffic() is not None
-    hk = bench.hbm_kernel_traffic()
-    assert set(hk) == {"adaln1", "adaln2", "quant_o", "quant_g"}
-    # counters within a few percent of the algorithmic bytes of these kernels
-    alg = bench.hbm_bytes(4352, 4096, 16384)
-    for site, b in hk.items():
-        assert 1.0 <= b / alg[site] < 1.05
+def _tree(tmp_path, sources):
     csrc = tmp_path / "diffusion_transformer_text_qwen_amd" / "csrc"
     csrc.mkdir(parents=True)
     (tmp_path / "profiles").mkdir()
     for name in ("gemm_w8a8_1024px_traffic.json", "hbm_kernels_1024px_traffic.json"):
         (tmp_path / "profiles" / name).write_text(open(os.path.join(bench.ROOT, "profiles", name)).read())
-    (csrc / "gemm.hip").write_text("// changed\n")
-    (csrc / "elementwise.hip").write_text("// changed\n")
-    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for name, text in sources.items():
+        (csrc / name).write_bytes(text)
+    return str(tmp_path)
+
+
+def test_counter_traffic_tracks_the_sources(tmp_path, monkeypatch):
+    """Counter bytes are reported only for the source they were taken with: a
+    tree whose sources hash as recorded reports them, any other reports none."""
+    gt = json.load(open(os.path.join(bench.ROOT, "profiles", "gemm_w8a8_1024px_traffic.json")))
+    ht = json.load(open(os.path.join(bench.ROOT, "profiles", "hbm_kernels_1024px_traffic.json")))
+    # the HBM-bound kernels' counters lie within a few percent of their algorithmic bytes
+    alg = bench.hbm_bytes(4352, 4096, 16384)
+    site = {"adaln": "adaln1", "quant_o": "quant_o", "quant_g": "quant_g"}
+    for k, v in ht["kernels"].items():
+        assert 1.0 <= (v["bytes_read"] + v["bytes_written"]) / alg[site[k]] < 1.05
+    # a source that does not hash as recorded: no traffic
+    monkeypatch.setattr(bench, "ROOT", _tree(tmp_path / "a", {"gemm.hip": b"// changed\n",
+                                                              "elementwise.hip": b"// changed\n"}))
     assert bench.gemm_traffic() is None
     assert bench.hbm_kernel_traffic() == {}
+    # sources that hash as recorded (stand-ins with the recorded digests patched in)
+    real_sha = bench.hashlib.sha256
+    digests = {b"G": gt["gemm_source_sha256"], b"E": ht["elementwise_source_sha256"]}
+
+    class _Fake:
+        def __init__(self, data):
+            self.d = digests.get(data)
+            self.r = real_sha(data)
+
+        def hexdigest(self):
+            return self.d or self.r.hexdigest()
+    monkeypatch.setattr(bench.hashlib, "sha256", _Fake)
+    monkeypatch.setattr(bench, "ROOT", _tree(tmp_path / "b", {"gemm.hip": b"G", "elementwise.hip": b"E"}))
+    want = gt["fetch_kib_per_launch"] * 1024 / gt["copy_fetch_per_byte"] + \
+        gt["write_kib_per_launch"] * 1024 / gt["copy_write_per_byte"]
+    assert bench.gemm_traffic() == int(want)
+    hk = bench.hbm_kernel_traffic()
+    assert set(hk) == {"adaln1", "adaln2", "quant_o", "quant_g"}
+    assert hk["quant_g"] == ht["kernels"]["quant_g"]["bytes_read"] + ht["kernels"]["quant_g"]["bytes_written"]
