@@ -107,6 +107,7 @@ _SIGS = {
                           _c_i64, _vp], ctypes.c_int),
     "dit_adaln_modulate": ([_vp, ctypes.c_int, _c_i64, _c_i64, _vp, _vp, _fp, _vp, ctypes.c_int, _vp, _vp,
                             _vp], ctypes.c_int),
+    "dit_adaln_modulate_asym": ([_vp, _c_i64, _c_i64, _vp, _vp, _fp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "dit_euler_step": ([_vp, _vp, ctypes.c_int, _c_i64, _fp, _fp, _vp], ctypes.c_int),
     "dit_cast": ([_vp, ctypes.c_int, _vp, ctypes.c_int, _c_i64, _vp], ctypes.c_int),
     "dit_profile_begin": ([_c_i32], ctypes.c_int),
@@ -330,6 +331,13 @@ def adaln_modulate(x, shift, scale, h_out=None, q_out=None, q_scale=None, eps: f
     hdt = _dt(h_out) if h_out is not None else _dt(x)
     _check(lib().dit_adaln_modulate(_p(x), _dt(x), M, D, _p(shift), _p(scale), eps, _p(h_out), hdt,
                                     _p(q_out), _p(q_scale), _stream(stream)), "dit_adaln_modulate")
+
+
+def adaln_modulate_asym(x, shift, scale, q_out, q_scale, q_zero, h_out=None, eps: float = 1e-6,
+                        stream=None) -> None:
+    M, D = x.shape
+    _check(lib().dit_adaln_modulate_asym(_p(x), M, D, _p(shift), _p(scale), eps, _p(h_out), _p(q_out),
+                                         _p(q_scale), _p(q_zero), _stream(stream)), "dit_adaln_modulate_asym")
 
 
 def euler_step(x, v, sigma: float, sigma_next: float, stream=None) -> None:

@@ -530,6 +530,27 @@ int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const f
     return DIT_OK;
 }
 
+int dit_adaln_modulate_asym(const void* x, int64_t M, int64_t D, const float* shift, const float* scale,
+                            float eps, void* h_out, int8_t* q_out, float* q_scale, int32_t* q_zero,
+                            void* stream) {
+    CHECK(M >= 0 && D >= 256, DIT_E_SHAPE, "need M>=0, D>=256");
+    CHECK(D % 256 == 0 && D <= 4096, DIT_E_UNSUPPORTED, "D must be a multiple of 256, <= 4096");
+    CHECK(M <= 0x7fffffff, DIT_E_UNSUPPORTED, "M too large");
+    if (M == 0) return DIT_OK;
+    CHECK(x && shift && scale && q_out && q_scale && q_zero, DIT_E_NULL,
+          "x, shift, scale, q_out, q_scale and q_zero must be non-NULL");
+    CHECK(aligned16(x) && aligned16(shift) && aligned16(scale) && (!h_out || aligned16(h_out)) &&
+              ((uintptr_t)q_out & 7) == 0,
+          DIT_E_ALIGN, "x, shift, scale and h_out must be 16-byte aligned, q_out 8-byte aligned");
+    SegMap sm{};
+    sm.end[0] = M;
+    sm.set[0] = 0;
+    sm.n = 1;
+    RUN(launch_adaln_asym(x, M, D, shift, scale, 0, sm, eps, h_out, q_out, q_scale, q_zero, S(stream)),
+        "adaln_asym");
+    return DIT_OK;
+}
+
 int dit_euler_step(float* x, const void* v, int v_dtype, int64_t n, float sigma, float sigma_next,
                    void* stream) {
     CHECK(v_dtype == DIT_BF16 || v_dtype == DIT_F32, DIT_E_DTYPE, "v_dtype must be bf16 or f32");
@@ -937,16 +958,24 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     auto quant = [&](const void* A, int64_t K) -> hipError_t {
         return launch_quantize_rows_asym(A, true, T, K, K, a8, sa, za, st);
     };
+    // adaLN prologue: h (bf16) when a bf16 or MXFP4 linear reads it, and the
+    // asymmetric codes of h when an int8 linear does (fused into the adaLN
+    // pass where its kernel takes the shape, else a second pass over h)
+    auto prologue = [&](const float* shift, const float* scale, const dit_linear& l1,
+                        const dit_linear& l2) -> hipError_t {
+        const bool need_q = l1.s || l2.s, need_h = !l1.s || !l2.s;
+        void* ho = need_h ? h : nullptr;
+        if (need_q && adaln_fuses_asym(D, mstride, x, shift, scale, ho, a8))
+            return launch_adaln_asym(x, T, D, shift, scale, mstride, sm, cfg->ln_eps, ho, a8, sa, za, st);
+        const hipError_t e = launch_adaln(x, true, T, D, shift, scale, mstride, sm, cfg->ln_eps, h, nullptr,
+                                          nullptr, st);
+        if (e != hipSuccess || !need_q) return e;
+        return quant(h, D);
+    };
 
     {
         ProfScope ps(DIT_SITE_ADALN1, st);
-        RUN(launch_adaln(x, true, T, D, io->mod + 0 * D, io->mod + 1 * D, mstride, sm, cfg->ln_eps, h, nullptr,
-                         nullptr, st),
-            "adaln1");
-    }
-    if (w->qk.s || w->v.s) {
-        ProfScope ps(DIT_SITE_ADALN1, st);
-        RUN(quant(h, D), "quantize h");
+        RUN(prologue(io->mod + 0 * D, io->mod + 1 * D, w->qk, w->v), "adaln1");
     }
     {
         // Q/K: RMSNorm + RoPE in the GEMM epilogue (columns [0, D) q, [D, 2D) k)
@@ -999,13 +1028,7 @@ int gated_impl(const dit_block_config* cfg, const dit_gated_block_weights* w, co
     }
     {
         ProfScope ps(DIT_SITE_ADALN2, st);
-        RUN(launch_adaln(x, true, T, D, io->mod + 3 * D, io->mod + 4 * D, mstride, sm, cfg->ln_eps, h, nullptr,
-                         nullptr, st),
-            "adaln2");
-    }
-    if (w->proj.s || w->gate.s) {
-        ProfScope ps(DIT_SITE_ADALN2, st);
-        RUN(quant(h, D), "quantize h2");
+        RUN(prologue(io->mod + 3 * D, io->mod + 4 * D, w->proj, w->gate), "adaln2");
     }
     {
         // gated MLP: u = proj(h2) (bf16), then g = u * GELU(gate(h2)) in the gate GEMM's epilogue

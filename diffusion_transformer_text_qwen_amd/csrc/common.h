@@ -194,6 +194,46 @@ __device__ __forceinline__ uint2 quant8(const float (&v)[8], float s, float inv,
     return o;
 }
 
+// Asymmetric int8 code of x for scale s and zero point z:
+// clamp(rint(x / s) + z, -128, 127) with an IEEE division, 0 when s == 0.
+__device__ __forceinline__ int asym_code(float x, float s, int z) {
+    if (s == 0.0f) return 0;
+    const int r = (int)rintf(__fdiv_rn(x, s)) + z;
+    return min(max(r, -128), 127);
+}
+
+// asym_code of 8 values of a row whose range [lo, hi] (containing 0) gave
+// s = fl((hi - lo) / 255): |x / s| <= 255.01, so t = fl(x * inv) (inv = fl(1/s))
+// lies within 5e-5 of fl(x / s) and rounds to the same integer unless it is
+// that close to a half-integer; chunks with any t within 1e-4 of one, and
+// fast == false (s tiny or zero), take the IEEE division.
+__device__ __forceinline__ uint2 quant8_asym(const float (&v)[8], float s, float inv, int z, bool fast) {
+    constexpr float kMagic = 12582912.0f;   // 1.5 * 2^23
+    int b[8];
+    float dev = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float t = v[e] * inv;
+        const float m = t + kMagic;
+        dev = fmaxf(dev, fabsf(t - (m - kMagic)));
+        b[e] = min(max(__builtin_bit_cast(int, m) - 0x4B400000 + z, -128), 127);
+    }
+    if (__builtin_expect(__any(!fast || !(dev < 0.4999f)), 0)) {
+        if (!fast || !(dev < 0.4999f)) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b[e] = asym_code(v[e], s, z);
+        }
+    }
+    const uint32_t p01 = __builtin_amdgcn_perm((uint32_t)b[1], (uint32_t)b[0], 0x0c0c0400u);
+    const uint32_t p23 = __builtin_amdgcn_perm((uint32_t)b[3], (uint32_t)b[2], 0x0c0c0400u);
+    const uint32_t p45 = __builtin_amdgcn_perm((uint32_t)b[5], (uint32_t)b[4], 0x0c0c0400u);
+    const uint32_t p67 = __builtin_amdgcn_perm((uint32_t)b[7], (uint32_t)b[6], 0x0c0c0400u);
+    uint2 o;
+    o.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);
+    o.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);
+    return o;
+}
+
 // Raw buffer resource over `bytes` bytes at p: loads past the end read zero,
 // stores past the end are dropped (bounds handled without branches).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* p, int bytes) {

@@ -262,13 +262,15 @@ __global__ void __launch_bounds__(256) adaln_kernel(const T* __restrict__ x, int
 // bf16 rows of width D <= 512 * MAXC, one wave per row (four per workgroup):
 // the row is held as packed bf16 pairs, mean, variance and amax are DPP wave
 // reductions, and the modulation vectors are read 16 bytes at a time.
-template <int MAXC>
+// ASYM: the codes of h are asymmetric (range [min(h, 0), max(h, 0)], zero
+// points to qz), as the W8A8 recipe's activations are.
+template <int MAXC, bool ASYM>
 __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restrict__ x, int64_t M, int D,
                                                          const float* __restrict__ shift0,
                                                          const float* __restrict__ scale0,
                                                          int64_t mod_stride, SegMap sm, float eps,
                                                          __bf16* __restrict__ h, int8_t* __restrict__ qo,
-                                                         float* __restrict__ qs) {
+                                                         float* __restrict__ qs, int32_t* __restrict__ qz) {
     const int lane = threadIdx.x % kWave;
     // wave-uniform row (an SGPR): buffer resources built from it then need no
     // per-lane waterfall loop around each load and store
@@ -301,7 +303,7 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
             }
     const float var = wave_allsum(ss) / (float)D;
     const float rstd = 1.0f / sqrtf(var + eps);
-    float amax = 0.0f;
+    float amax = 0.0f, hmin = 0.0f;   // amax: max |h| (symmetric) or max(h, 0) (ASYM)
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int c = i * kWave + lane;
@@ -317,7 +319,12 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
                 const float lo = (bf_lo(buf[i][w]) - mean) * rstd * (1.0f + scv[2 * w]) + shv[2 * w];
                 const float hi = (bf_hi(buf[i][w]) - mean) * rstd * (1.0f + scv[2 * w + 1]) + shv[2 * w + 1];
                 buf[i][w] = bf_pack(lo, hi);
-                amax = fmaxf(amax, fmaxf(fabsf(bf_lo(buf[i][w])), fabsf(bf_hi(buf[i][w]))));
+                if constexpr (ASYM) {
+                    amax = fmaxf(amax, fmaxf(bf_lo(buf[i][w]), bf_hi(buf[i][w])));
+                    hmin = fminf(hmin, fminf(bf_lo(buf[i][w]), bf_hi(buf[i][w])));
+                } else {
+                    amax = fmaxf(amax, fmaxf(fabsf(bf_lo(buf[i][w])), fabsf(bf_hi(buf[i][w]))));
+                }
             }
         }
         opaque(buf[i]);
@@ -329,7 +336,16 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
     }
     if (qo == nullptr) return;
     amax = wave_allmax(amax);
-    const float sq = __fdiv_rn(amax, 127.0f);
+    int z = 0;
+    float sq;
+    if constexpr (ASYM) {
+        hmin = -wave_allmax(-hmin);
+        sq = __fdiv_rn(amax - hmin, 255.0f);
+        if (sq != 0.0f) z = min(max(-128 - (int)rintf(__fdiv_rn(hmin, sq)), -128), 127);
+        if (lane == 0) qz[row] = z;
+    } else {
+        sq = __fdiv_rn(amax, 127.0f);
+    }
     if (lane == 0) qs[row] = sq;
     const float inv = __fdiv_rn(1.0f, sq);
     const bool fast = sq >= 0x1p-100f;
@@ -342,11 +358,30 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
             v[2 * w] = bf_lo(buf[i][w]);
             v[2 * w + 1] = bf_hi(buf[i][w]);
         }
-        buf_store8(quant8(v, sq, inv, fast), qr, (i * kWave + lane) * 8);
+        if constexpr (ASYM)
+            buf_store8(quant8_asym(v, sq, inv, z, fast), qr, (i * kWave + lane) * 8);
+        else
+            buf_store8(quant8(v, sq, inv, fast), qr, (i * kWave + lane) * 8);
     }
 }
 
 static bool al16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+bool adaln_fuses_asym(int64_t D, int64_t mod_stride, const void* x, const void* shift, const void* scale,
+                      const void* h, const void* qo) {
+    return D % 8 == 0 && D <= 4096 && mod_stride % 4 == 0 && al16(x) && al16(shift) && al16(scale) &&
+           ((uintptr_t)qo & 7) == 0 && (h == nullptr || al16(h));
+}
+
+hipError_t launch_adaln_asym(const void* x, int64_t M, int64_t D, const float* shift, const float* scale,
+                             int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo, float* qs,
+                             int32_t* qz, hipStream_t st) {
+    if (M == 0) return hipSuccess;
+    if (!adaln_fuses_asym(D, mod_stride, x, shift, scale, h, qo)) return hipErrorInvalidValue;
+    adaln_wave_kernel<8, true><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
+        (const __bf16*)x, M, (int)D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs, qz);
+    return hipGetLastError();
+}
 
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                         const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
@@ -354,8 +389,8 @@ hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const fl
     if (M == 0) return hipSuccess;
     if (bf16 && D % 8 == 0 && D <= 4096 && mod_stride % 4 == 0 && al16(x) && al16(shift) && al16(scale) &&
         (qo == nullptr || ((uintptr_t)qo & 7) == 0) && (h == nullptr || al16(h))) {
-        adaln_wave_kernel<8><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
-            (const __bf16*)x, M, (int)D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs);
+        adaln_wave_kernel<8, false><<<dim3((unsigned)((M + 3) / 4)), dim3(256), 0, st>>>(
+            (const __bf16*)x, M, (int)D, shift, scale, mod_stride, sm, eps, (__bf16*)h, qo, qs, nullptr);
         return hipGetLastError();
     }
     // D % 2048 != 0 (e.g. 512) is handled by VPT=8 with nvec = D/2048 == 0 -> use

@@ -36,12 +36,6 @@ __device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
            ((uint32_t)(d & 0xFF) << 24);
 }
 
-__device__ __forceinline__ int asym_code(float x, float s, int z) {
-    if (s == 0.0f) return 0;
-    const int r = (int)rintf(__fdiv_rn(x, s)) + z;
-    return min(max(r, -128), 127);
-}
-
 // One workgroup per row; 8 consecutive values per thread and pass (K % 8 == 0).
 template <typename T>
 __global__ void __launch_bounds__(256) quant_asym_kernel(const T* __restrict__ x, int64_t ldx, int64_t K,

@@ -92,6 +92,13 @@ hipError_t launch_gelu_quantize_rows(const void* u, int64_t M, int64_t K, int8_t
 hipError_t launch_adaln(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                         const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
                         float* qs, hipStream_t st);
+// bf16 x, D <= 4096: h (if not NULL) and the asymmetric int8 codes of h
+// (qo, qs, zero points qz), as launch_quantize_rows_asym would form them from h.
+bool adaln_fuses_asym(int64_t D, int64_t mod_stride, const void* x, const void* shift, const void* scale,
+                      const void* h, const void* qo);
+hipError_t launch_adaln_asym(const void* x, int64_t M, int64_t D, const float* shift, const float* scale,
+                             int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo, float* qs,
+                             int32_t* qz, hipStream_t st);
 hipError_t launch_adaln_small(const void* x, bool bf16, int64_t M, int64_t D, const float* shift,
                               const float* scale, int64_t mod_stride, const SegMap& sm, float eps, void* h, int8_t* qo,
                               float* qs, hipStream_t st);

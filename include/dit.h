@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define DIT_ABI_VERSION 4
+#define DIT_ABI_VERSION 5
 
 typedef enum {
     DIT_OK = 0,
@@ -300,6 +300,20 @@ int dit_qk_norm_rope(const void* qkv, int dtype, int64_t T, int32_t H, const flo
 int dit_adaln_modulate(const void* x, int x_dtype, int64_t M, int64_t D, const float* shift,
                        const float* scale, float eps, void* h_out, int h_dtype, int8_t* q_out,
                        float* q_scale, void* stream);
+
+/*
+ * The adaLN prologue with the activation codes of the W8A8 recipe ("Qwen-Image-2.1
+ * W8A8 - FlagOS for Mac", Quantization and validation: dynamic asymmetric
+ * per-token int8 activations): h as in dit_adaln_modulate (bf16 x, bf16 h),
+ * written to h_out when it is not NULL, and h quantized per row exactly as
+ * dit_quantize_rows_asym quantizes it (q_out [M, D] int8, q_scale [M] fp32,
+ * q_zero [M] int32), in one pass over x.  Supported: D % 256 == 0, D <= 4096;
+ * x and h_out 16-byte aligned, q_out 8-byte aligned; else DIT_E_UNSUPPORTED or
+ * DIT_E_ALIGN before any launch.
+ */
+int dit_adaln_modulate_asym(const void* x, int64_t M, int64_t D, const float* shift, const float* scale,
+                            float eps, void* h_out, int8_t* q_out, float* q_scale, int32_t* q_zero,
+                            void* stream);
 
 /* FlowMatch Euler update ("RGBA-Image-2.1 - Core AI port", Graph contracts,
  * Sampler): x[i] += (sigma_next - sigma) * v[i] in fp32; x fp32, v bf16 or f32. */

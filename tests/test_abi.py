@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(dq.exported_symbols())
-    assert lib.dit_abi_version() == 4
+    assert lib.dit_abi_version() == 5
 
 
 def test_status_strings():
@@ -109,6 +109,12 @@ def test_rope_and_misc_validation():
     assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, NULL, dq.BF16, NULL, NULL, S) == 1
     assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 24, dq.BF16, 16, 16, S) == 4
     assert lib.dit_adaln_modulate(16, dq.BF16, 4, 512, 16, 16, 1e-6, 16, dq.BF16, 16, NULL, S) == 1
+    # adaLN with asymmetric codes: D range, NULL outputs, alignment of h and q
+    assert lib.dit_adaln_modulate_asym(16, 4, 8192, 16, 16, 1e-6, 16, 16, 16, 16, S) == 5
+    assert lib.dit_adaln_modulate_asym(16, 4, 300, 16, 16, 1e-6, 16, 16, 16, 16, S) == 5
+    assert lib.dit_adaln_modulate_asym(16, 4, 512, 16, 16, 1e-6, 16, 16, 16, NULL, S) == 1
+    assert lib.dit_adaln_modulate_asym(16, 4, 512, 16, 16, 1e-6, 24, 16, 16, 16, S) == 4
+    assert lib.dit_adaln_modulate_asym(16, 4, 512, 16, 16, 1e-6, NULL, 20, 16, 16, S) == 4
 
 
 def test_gelu_quantize_validation():

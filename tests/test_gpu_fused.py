@@ -178,6 +178,43 @@ def test_adaln_fused_codes_bit_exact(M, D):
     assert np.mean(hg == oracle.round_bf16(ref)) > 0.99
 
 
+@pytest.mark.parametrize("M,D", [(100, 4096), (4352, 4096), (37, 512), (29, 1024)])
+def test_adaln_fused_asym_codes_bit_exact(M, D):
+    """The adaLN pass with the W8A8 recipe's asymmetric activation codes: codes,
+    scales and zero points equal the oracle's asymmetric quantization of the
+    kernel's own h bit for bit, h is the oracle's adaLN within one bf16 rounding,
+    and the launch without h_out writes the same codes."""
+    say("adaln fused asym codes", M, D)
+    rng = np.random.default_rng(M * 3 + D)
+    x = (rng.standard_normal((M, D)) * 2 + 0.5).astype(np.float32)
+    x[M // 2] *= 40.0                                   # a large-amplitude row
+    x[M // 3] = 1.5                                     # a constant row: h = shift
+    x = ditsynth.to_bf16_grid(x)
+    shift = (rng.standard_normal(D) * 0.7).astype(np.float32)
+    scale = (rng.standard_normal(D) * 0.7).astype(np.float32)
+    args = (dev(x, torch.bfloat16), dev(shift), dev(scale))
+    h = torch.empty((M, D), dtype=torch.bfloat16, device=DEV)
+    out = []
+    for h_out in (h, None):
+        q = torch.full((M, D), 99, dtype=torch.int8, device=DEV)
+        qs = torch.empty(M, dtype=torch.float32, device=DEV)
+        qz = torch.empty(M, dtype=torch.int32, device=DEV)
+        dq.adaln_modulate_asym(*args, q, qs, qz, h_out=h_out)
+        out.append((q, qs, qz))
+    torch.cuda.synchronize()
+    hg = host(h)
+    q_ref, s_ref, z_ref = oracle.quantize_rows_asym(hg)
+    for q, qs, qz in out:
+        assert np.array_equal(qs.cpu().numpy(), s_ref)
+        assert np.array_equal(qz.cpu().numpy(), z_ref)
+        assert np.array_equal(q.cpu().numpy(), q_ref)
+    ref = oracle.adaln_modulate(x, shift, scale)
+    assert np.all(np.abs(hg - ref) <= bf16_ulp(ref) + 1e-6)
+    assert np.mean(hg == oracle.round_bf16(ref)) > 0.99
+    # the codes span the int8 range: the row minimum maps to -128
+    assert (q_ref.min(axis=1) == -128).mean() > 0.9
+
+
 @pytest.mark.parametrize("M,K", [(300, 16384), (97, 4096), (33, 12288), (5, 1032)])
 def test_gelu_quantize_bit_exact(M, K):
     """g = bf16(GELU_tanh(u)) within one bf16 ulp of the oracle (>= 99.9% equal),
