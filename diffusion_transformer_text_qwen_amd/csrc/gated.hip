@@ -31,11 +31,6 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
     }
 }
 
-__device__ __forceinline__ uint32_t pack4(int a, int b, int c, int d) {
-    return (uint32_t)(a & 0xFF) | ((uint32_t)(b & 0xFF) << 8) | ((uint32_t)(c & 0xFF) << 16) |
-           ((uint32_t)(d & 0xFF) << 24);
-}
-
 // One workgroup per row; 8 consecutive values per thread and pass (K % 8 == 0).
 template <typename T>
 __global__ void __launch_bounds__(256) quant_asym_kernel(const T* __restrict__ x, int64_t ldx, int64_t K,
@@ -67,13 +62,12 @@ __global__ void __launch_bounds__(256) quant_asym_kernel(const T* __restrict__ x
     const float s = __fdiv_rn(hi - lo, 255.0f);
     const int z = s == 0.0f ? 0 : min(max(-128 - (int)rintf(__fdiv_rn(lo, s)), -128), 127);
     int8_t* qr = q + row * K;
+    const float inv = __fdiv_rn(1.0f, s);
+    const bool fast = s >= 0x1p-100f;
     for (int64_t k = (int64_t)tid * 8; k < K; k += 256 * 8) {
         float v[8];
         load8(xr + k, v);
-        uint2 o;
-        o.x = pack4(asym_code(v[0], s, z), asym_code(v[1], s, z), asym_code(v[2], s, z), asym_code(v[3], s, z));
-        o.y = pack4(asym_code(v[4], s, z), asym_code(v[5], s, z), asym_code(v[6], s, z), asym_code(v[7], s, z));
-        *reinterpret_cast<uint2*>(qr + k) = o;
+        *reinterpret_cast<uint2*>(qr + k) = quant8_asym(v, s, inv, z, fast);
     }
     if (tid == 0) {
         scale[row] = s;

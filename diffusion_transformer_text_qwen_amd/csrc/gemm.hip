@@ -362,6 +362,12 @@ gemm_mfma_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __
 constexpr int L_BM = 256, L_BN = 256, L_BK = 64, L_SK = 128, L_SLOTS = 2, L_THREADS = 512;
 constexpr int L_TILE_BYTES = L_BM * L_SK;               // one operand, one slot
 constexpr int L_STAGE_BYTES = 2 * L_TILE_BYTES;
+// Epilogue LDS: two slab buffers of 8 waves x 16 rows x (wave tile width + 4)
+// words (at most 128 + 4 wide), then the tile's epilogue constants: weight
+// scales [256], bias [256] and activation scales [256] (fp32), loaded into LDS
+// with the operand prologue.
+constexpr int L_CONST = 2 * 8 * 16 * (128 + 4) * 4;
+constexpr int L_CONST_BYTES = 3 * 1024;
 
 
 // Partial last round: with T tiles on C compute units, the C workgroups of one
@@ -592,6 +598,24 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
         }
     }
 
+    // the epilogue's column and row constants of a whole tile go to LDS ahead of
+    // the operands (wave 0; the prologue's first wait covers them: loads land
+    // in issue order); columns or rows past N or M read as zero
+    if (part == nullptr && __builtin_amdgcn_readfirstlane(wave) == 0) {
+        if constexpr (I8) {
+            const auto rw = __builtin_amdgcn_make_buffer_rsrc((void*)ep.w_scale, 0, (int)(N * 4), 0x00020000);
+            const auto ra = __builtin_amdgcn_make_buffer_rsrc((void*)ep.a_scale, 0, (int)(M * 4), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(lds + L_CONST), 16, (int)(n0 * 4) + lane * 16,
+                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + L_CONST + 2048), 16,
+                                                     (int)(m0 * 4) + lane * 16, 0, 0, 0);
+        }
+        if (ep.bias != nullptr) {
+            const auto rb = __builtin_amdgcn_make_buffer_rsrc((void*)ep.bias, 0, (int)(N * 4), 0x00020000);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + L_CONST + 1024), 16,
+                                                     (int)(n0 * 4) + lane * 16, 0, 0, 0);
+        }
+    }
     // prologue: stages 0 and 1 in flight, wait for 0, fragments of step 0
     if constexpr (W4) {
         // codes of stages 0 and 1 decoded before the first barrier, those of
@@ -670,93 +694,84 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     }
 
     // Epilogue: for each 16-row slab i, every wave parks its 16 x WTN slab of
-    // accumulators in its own LDS region, then each lane finishes 16
-    // consecutive columns of one row (LPR lanes per row, RPP rows per pass).
+    // accumulators in its own LDS region (two buffers: slab i+1 is parked
+    // while slab i is finished), then each lane finishes 16 consecutive
+    // columns of one row (LPR lanes per row, RPP rows per pass).
     constexpr int EP_STRIDE = WTN + 4;   // words per slab row (padded)
     constexpr int LPR = WTN / 16, RPP = kWave / LPR;
-    float* slab = reinterpret_cast<float*>(lds) + wave * 16 * EP_STRIDE;
+    static_assert(2 * 8 * 16 * EP_STRIDE * 4 <= L_CONST, "slab buffers");
+    float* const slab_buf[2] = {reinterpret_cast<float*>(lds) + wave * 16 * EP_STRIDE,
+                                reinterpret_cast<float*>(lds) + (8 + wave) * 16 * EP_STRIDE};
     const int er0 = lane / LPR, ec = (lane % LPR) * 16;
     const int64_t n = n0 + wn * WTN + ec;
     QkvAux aux;
     if constexpr (EV == EV_QKV) {
         qkv_gain16(ep, n, aux);
     }
-    // Per-lane column constants (weight scales, bias) and the row scales of
-    // every slab are loaded once, before the first slab, so that no slab
-    // waits on a global load of its own.
-    constexpr int NPASS = 16 / RPP;
-    float colw[16], colb[16], rows_sa[MF][NPASS];
-    {
-        const bool cb = n < N && ep.bias != nullptr;
+    // column constants (weight scales, bias) from the tile's LDS copy
+    const float* cl = reinterpret_cast<const float*>(lds + L_CONST);
+    float colw[16], colb[16];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const v4f b4 = cb ? *reinterpret_cast<const v4f*>(ep.bias + n + 4 * q) : v4f{0.f, 0.f, 0.f, 0.f};
-            v4f w4 = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (I8) {
-                if (n < N) w4 = *reinterpret_cast<const v4f*>(ep.w_scale + n + 4 * q);
-            }
+    for (int q = 0; q < 4; ++q) {
+        const v4f w4 = I8 ? *reinterpret_cast<const v4f*>(cl + wn * WTN + ec + 4 * q) : v4f{1.f, 1.f, 1.f, 1.f};
+        const v4f b4 = ep.bias != nullptr ? *reinterpret_cast<const v4f*>(cl + 256 + wn * WTN + ec + 4 * q)
+                                          : v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                colb[4 * q + e] = b4[e];
-                colw[4 * q + e] = w4[e];
-            }
+        for (int e = 0; e < 4; ++e) {
+            colw[4 * q + e] = w4[e];
+            colb[4 * q + e] = b4[e];
         }
     }
-    if constexpr (I8) {
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-            for (int pass = 0; pass < NPASS; ++pass) {
-                const int64_t m = m0 + wm * WTM + i * 16 + pass * RPP + er0;
-                rows_sa[i][pass] = m < M ? ep.a_scale[m] : 0.0f;
-            }
-    }
-#pragma unroll
-    for (int i = 0; i < MF; ++i) {
+    auto park = [&](int i) {
+        float* sl = slab_buf[i & 1];
 #pragma unroll
         for (int j = 0; j < NF; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 if constexpr (I8)
-                    reinterpret_cast<int32_t*>(slab)[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] =
+                    reinterpret_cast<int32_t*>(sl)[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] =
                         acc[i][j][r];
                 else
-                    slab[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
+                    sl[((lane / 16) * 4 + r) * EP_STRIDE + j * 16 + lane % 16] = acc[i][j][r];
             }
-        // a wave's LDS accesses execute in order: no wait between its slab writes
-        // and reads (the empty asm keeps the compiler from reordering them)
-        asm volatile("" ::: "memory");
+    };
+    park(0);
+#pragma unroll
+    for (int i = 0; i < MF; ++i) {
+        const float* slab = slab_buf[i & 1];
 #pragma unroll
         for (int pass = 0; pass < 16 / RPP; ++pass) {
             const int er = pass * RPP + er0;
             const int64_t m = m0 + wm * WTM + i * 16 + er;
+            // this row's 16 accumulators (and its activation scale) first, then
+            // slab i+1 is parked while they are finished: a wave's LDS accesses
+            // execute in order, so the writes wait behind these reads only, and
+            // slab i's buffer is parked again only after its last reads
+            acc_t t[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t[q] = *reinterpret_cast<const acc_t*>(slab + er * EP_STRIDE + ec + 4 * q);
+            const float sa = I8 ? cl[512 + wm * WTM + i * 16 + er] : 1.0f;
+            if (pass == 0 && i + 1 < MF) {
+                asm volatile("" ::: "memory");
+                park(i + 1);
+            }
             float v[16];
             int32_t ai[16];
             const bool ok = m < M && n < N;
             if (ok) {
-                if constexpr (I8) {
-                    const float sa = rows_sa[i][pass];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        // (zero-point correction, if any, is already in the accumulators)
-                        const v4i t = *reinterpret_cast<const v4i*>(
-                            reinterpret_cast<const int32_t*>(slab) + er * EP_STRIDE + ec + 4 * q);
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            ai[4 * q + e] = t[e];
-                            v[4 * q + e] = (float)t[e] * sa * colw[4 * q + e];
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (I8) {
+                            // (zero-point correction, if any, is already in the accumulators)
+                            ai[4 * q + e] = t[q][e];
+                            v[4 * q + e] = (float)t[q][e] * sa * colw[4 * q + e];
+                        } else {
+                            ai[4 * q + e] = 0;
+                            v[4 * q + e] = t[q][e];
                         }
                     }
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const v4f t = *reinterpret_cast<const v4f*>(slab + er * EP_STRIDE + ec + 4 * q);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) v[4 * q + e] = t[e];
-                    }
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) ai[e] = 0;
-                }
             }
             if constexpr (EV == EV_QKV) {
                 // a head's 128 columns are this wave's 8 lanes of the row
@@ -839,7 +854,8 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
 }
 
 constexpr int kNumCU = 256;
-constexpr size_t L_LDS = (size_t)L_SLOTS * L_STAGE_BYTES;
+constexpr size_t L_LDS = (size_t)std::max(L_SLOTS * L_STAGE_BYTES, L_CONST + L_CONST_BYTES);
+static_assert(L_LDS <= 160 * 1024, "LDS per workgroup");
 
 // The 256 x 256 persistent kernel takes a shape when its tiles, or their K-split
 // ranges, occupy at least three quarters of the compute units; smaller shapes
