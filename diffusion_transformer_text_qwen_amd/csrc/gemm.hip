@@ -376,8 +376,8 @@ constexpr int L_CONST_BYTES = 3 * 1024;
 // stores its partial sums (int32 for int8 operands, fp32 for bf16).  A second
 // launch adds the partials (int32: exact in any order; fp32: in K order) and
 // applies the epilogue; the kernel boundary orders the partial stores before
-// their reads.  The K range runs before the whole tiles, so its
-// partial stores overlap them.  For long K loops (more than 64 steps) two
+// their reads.  On half the XCDs the K range runs before the whole tiles (its
+// partial stores overlap them), on the other half after them.  For long K loops (more than 64 steps) two
 // launches measured faster: whole tiles, then the K ranges (the same kernel
 // with full = 0).
 struct LargePlan {
@@ -818,11 +818,15 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
     // G per job.  Workgroups are dealt round-robin to the 8 XCDs; with full a
     // multiple of G, XCD x takes the contiguous tile range [x full/8,
     // (x+1) full/8) so that tiles sharing rows of A or W share an L2.  One call
-    // site keeps one copy of the tile code.
+    // site keeps one copy of the tile code.  The even XCDs take their K range
+    // first and the odd ones last, so the two halves of the chip run their
+    // whole tiles a K range out of phase: the epilogues' output stores, which
+    // saturate the write path when every CU stores its tile at once, come in
+    // two bursts of half the size.
     const bool chunk = lp.S > 0 && b < lp.r * lp.S;
     const bool xcd = G % 8 == 0 && lp.full % G == 0;
     const int jobs = (lp.full + G - 1) / G;
-    const int cj = chunk ? 0 : -1;   // job index of the K range
+    const int cj = chunk ? ((b & 1) ? jobs : 0) : -1;   // job index of the K range
     for (int j = 0; j < jobs + (chunk ? 1 : 0); ++j) {
         // keep the epilogue's parameter loads inside the loop (hoisting them
         // would hold them in registers across the main loop)
