@@ -168,110 +168,124 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                     if (key >= my_end) scur[kh][j] = -INFINITY;
                 }
         }
-        const float mb = m_run * c_log2;
-        // Scores of tile t+1 interleaved with P of tile t: MFMA i (key half
-        // i % 2, k-block i / 2) with its operand read four ahead and P of two
-        // scores; sched_barrier keeps each group where it is written.
+        // P of scores e, e+1 (bf16, as the PV MFMA takes them) against the
+        // reference mref; the row sum adds the same rounded values with one dot2
+        v8bf pb[4];
+        auto p_pair = [&](int e, float mref, float& ps) {
+            v2bf p2;
+            p2[0] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16], c_log2, -mref)));
+            p2[1] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16 + 1], c_log2, -mref)));
+            pb[e / 8][e % 8] = p2[0];
+            pb[e / 8][e % 8 + 1] = p2[1];
+            ps = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, ps, false);
+        };
+        // P of one key half was formed against the running max.  When a
+        // lane's sum over the half exceeds kRescaleMax (or is not finite),
+        // raise the running max to the half's max, rescale, and form that
+        // half's P again (a wave-uniform branch, taken on the first tile and
+        // on tiles whose scores climb well above all earlier ones).  O and l
+        // already hold the earlier P against the old max, so both are scaled.
+        auto settle = [&](int kh, float& ps) {
+            if (__any(!(ps <= kRescaleMax))) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kh][j]);
+                mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+                const float m_new = fmaxf(m_run, mx);
+                if (m_new > m_run) {
+                    const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
+                    l_run *= alpha;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
+                    m_run = m_new;
+                }
+                // a row with no visible key so far keeps P = 0
+                const float mb2 = m_run == -INFINITY ? 0.0f : m_run * c_log2;
+                ps = 0.0f;
+#pragma unroll
+                for (int e = 16 * kh; e < 16 * kh + 16; e += 2) p_pair(e, mb2, ps);
+            }
+            l_run += ps;
+        };
+        // Scores of tile t+1 interleaved with P of key half 0 of tile t (one
+        // score per MFMA), the LDS stores of K(t+2) and the loads of K(t+3):
+        // MFMA i (key half i % 2, k-block i / 2) with its operand read four
+        // ahead; sched_barrier keeps each group where it is written.
         auto kfrag = [&](int i) {
             return *reinterpret_cast<const v8bf*>(knext + ((i % 2) * 32 + lq) * KS_STRIDE + (i / 2) * 32 + hh * 16);
         };
         v8bf kf[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) kf[i] = kfrag(i);
+        const __amdgpu_buffer_rsrc_t krs = kv_rsrc(kbase, j0 + 3 * AK, T_k, ldk);
         snxt[0] = v16f{};
         snxt[1] = v16f{};
-        float psum = 0.0f;
-        v8bf pb[4];
+        float mb = m_run * c_log2;
+        float ps0 = 0.0f, ps1 = 0.0f;
+        float pe = 0.0f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (i + 4 < 16) kf[i + 4] = kfrag(i + 4);
             snxt[i % 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[i / 2], snxt[i % 2], 0, 0, 0);
-            {
-                // P of scores 2i, 2i+1 (bf16, as the PV MFMA takes them); the
-                // row sum adds the same rounded values with one dot2
-                const int e = 2 * i;
+            const float p = __builtin_amdgcn_exp2f(fmaf(scur[0][i], c_log2, -mb));
+            if (i % 2 == 0) {
+                pe = p;
+            } else {
                 v2bf p2;
-                p2[0] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16], c_log2, -mb)));
-                p2[1] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16 + 1], c_log2, -mb)));
-                pb[e / 8][e % 8] = p2[0];
-                pb[e / 8][e % 8 + 1] = p2[1];
-                psum = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, psum, false);
+                p2[0] = to_bf16(pe);
+                p2[1] = to_bf16(p);
+                pb[i / 8][i % 8 - 1] = p2[0];
+                pb[i / 8][i % 8] = p2[1];
+                ps0 = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, ps0, false);
             }
+            if (i % 4 == 1)
+                *reinterpret_cast<v4i*>(kfree + (kkey + 16 * (i / 4)) * KS_STRIDE + kch * 16) = rk[i / 4];
+            if (i % 4 == 2)
+                rk[i / 4] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(krs, koff, (i / 4) * 16 * ldk * 2, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // P was formed against the running max.  When a lane's sum over this
-        // tile exceeds kRescaleMax (or is not finite), raise the running max
-        // to the tile's max, rescale, and form P again (a wave-uniform branch,
-        // taken on the first tile and on tiles whose scores climb well above
-        // all earlier ones).
-        if (__any(!(psum <= kRescaleMax))) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, scur[kh][j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-            const float m_new = fmaxf(m_run, mx);
-            if (m_new > m_run) {
-                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c_log2);
-                l_run *= alpha;
-#pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) oacc[dt][j] *= alpha;
-                m_run = m_new;
-            }
-            // a row with no visible key so far keeps P = 0
-            const float mb2 = m_run == -INFINITY ? 0.0f : m_run * c_log2;
-            psum = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 32; e += 2) {
-                v2bf p2;
-                p2[0] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16], c_log2, -mb2)));
-                p2[1] = to_bf16(__builtin_amdgcn_exp2f(fmaf(scur[e / 16][e % 16 + 1], c_log2, -mb2)));
-                pb[e / 8][e % 8] = p2[0];
-                pb[e / 8][e % 8 + 1] = p2[1];
-                psum = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, psum, false);
-            }
-        }
-        l_run += psum;
+        settle(0, ps0);
         // O^T += V^T P^T (16 keys per MFMA in the S^T lane order; MFMA i: key
-        // block i / 4, d tile i % 4), operands read four ahead; the LDS stores
-        // of K(t+2) and V(t+1) and the loads of K(t+3), V(t+2) in between.
+        // block i / 4, d tile i % 4), operands read four ahead.  MFMAs 0-7
+        // (key half 0) run beside P of key half 1, two scores each; MFMAs 8-15
+        // beside the transposing LDS stores of V(t+1); the loads of V(t+2)
+        // follow.
         auto vfrag = [&](int i) {
             return *reinterpret_cast<const v8bf*>(vcur + vrd + (i % 4) * 32 * VT_STRIDE + (i / 4) * 32);
         };
         v8bf vf[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) vf[i] = vfrag(i);
-        const __amdgpu_buffer_rsrc_t krs = kv_rsrc(kbase, j0 + 3 * AK, T_k, ldk);
         const __amdgpu_buffer_rsrc_t vrs = kv_rsrc(vbase, j0 + 2 * AK, T_k, ldv);
         uint8_t* vdst = vnext + dc * 8 * VT_STRIDE + vpos * 2;
+        mb = m_run * c_log2;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 8; ++i) {
             if (i + 4 < 16) vf[i + 4] = vfrag(i + 4);
             oacc[i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb[i / 4], oacc[i % 4], 0, 0, 0);
-            if (i < 4) {
-                *reinterpret_cast<v4i*>(kfree + (kkey + 16 * i) * KS_STRIDE + kch * 16) = rk[i];
-            } else if (i < 12) {
+            p_pair(16 + 2 * i, mb, ps1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        settle(1, ps1);
+#pragma unroll
+        for (int i = 8; i < 16; ++i) {
+            if (i + 4 < 16) vf[i + 4] = vfrag(i + 4);
+            oacc[i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[i], pb[i / 4], oacc[i % 4], 0, 0, 0);
+            {
                 // transpose: 4 keys x 8 dims -> row d = dc*8 + r of 4 keys
-                const int r = i - 4, w = r / 2;
+                const int r = i - 8, w = r / 2;
                 const uint32_t sel = (r % 2) ? 0x07060302u : 0x05040100u;
                 uint2 packed;
                 packed.x = __builtin_amdgcn_perm((uint32_t)rv[1][w], (uint32_t)rv[0][w], sel);
                 packed.y = __builtin_amdgcn_perm((uint32_t)rv[3][w], (uint32_t)rv[2][w], sel);
                 *reinterpret_cast<uint2*>(vdst + r * VT_STRIDE) = packed;
-            } else if (i < 14) {
-#pragma unroll
-                for (int q = 2 * (i - 12); q < 2 * (i - 12) + 2; ++q)
-                    rk[q] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(krs, koff, q * 16 * ldk * 2, 0);
-            } else {
-#pragma unroll
-                for (int q = 2 * (i - 14); q < 2 * (i - 14) + 2; ++q)
-                    rv[q] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vrs, voff, q * ldv * 2, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rv[q] = (v4i)__builtin_amdgcn_raw_buffer_load_b128(vrs, voff, q * ldv * 2, 0);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         __builtin_amdgcn_s_barrier();
     };
