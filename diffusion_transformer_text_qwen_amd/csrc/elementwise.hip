@@ -284,11 +284,14 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
     v4i buf[MAXC];
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) buf[i] = buf_load16(xr, (i * kWave + lane) * 16);
+    // row sum straight from the packed pairs: one dot2 with (1, 1) per pair
+    const v2bf ones = {(__bf16)1.0f, (__bf16)1.0f};
     float s = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
 #pragma unroll
-        for (int w = 0; w < 4; ++w) s += bf_lo(buf[i][w]) + bf_hi(buf[i][w]);
+        for (int w = 0; w < 4; ++w)
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, (int)buf[i][w]), ones, s, false);
         opaque(buf[i]);
     }
     const float mean = wave_allsum(s) / (float)D;
@@ -303,7 +306,11 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
             }
     const float var = wave_allsum(ss) / (float)D;
     const float rstd = 1.0f / sqrtf(var + eps);
-    float amax = 0.0f, hmin = 0.0f;   // amax: max |h| (symmetric) or max(h, 0) (ASYM)
+    // amax: max |h| (symmetric) or max(h, 0) (ASYM), taken over the fp32
+    // values before their bf16 rounding and rounded once afterwards: rounding
+    // to nearest is monotonic and odd, so the max of the rounded values is the
+    // rounded max
+    float amax = 0.0f, hmin = 0.0f;
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
         const int c = i * kWave + lane;
@@ -320,10 +327,10 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
                 const float hi = (bf_hi(buf[i][w]) - mean) * rstd * (1.0f + scv[2 * w + 1]) + shv[2 * w + 1];
                 buf[i][w] = bf_pack(lo, hi);
                 if constexpr (ASYM) {
-                    amax = fmaxf(amax, fmaxf(bf_lo(buf[i][w]), bf_hi(buf[i][w])));
-                    hmin = fminf(hmin, fminf(bf_lo(buf[i][w]), bf_hi(buf[i][w])));
+                    amax = fmaxf(amax, fmaxf(lo, hi));
+                    hmin = fminf(hmin, fminf(lo, hi));
                 } else {
-                    amax = fmaxf(amax, fmaxf(fabsf(bf_lo(buf[i][w])), fabsf(bf_hi(buf[i][w]))));
+                    amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
                 }
             }
         }
@@ -335,11 +342,11 @@ __global__ void __launch_bounds__(256) adaln_wave_kernel(const __bf16* __restric
         for (int i = 0; i < MAXC; ++i) buf_store16(buf[i], hr, (i * kWave + lane) * 16);
     }
     if (qo == nullptr) return;
-    amax = wave_allmax(amax);
+    amax = (float)to_bf16(wave_allmax(amax));
     int z = 0;
     float sq;
     if constexpr (ASYM) {
-        hmin = -wave_allmax(-hmin);
+        hmin = (float)to_bf16(-wave_allmax(-hmin));
         sq = __fdiv_rn(amax - hmin, 255.0f);
         if (sq != 0.0f) z = min(max(-128 - (int)rintf(__fdiv_rn(hmin, sq)), -128), 127);
         if (lane == 0) qz[row] = z;
