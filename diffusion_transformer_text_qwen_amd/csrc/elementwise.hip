@@ -79,6 +79,9 @@ __global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16*
     v4i buf[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) buf[i] = buf_load16(xr, ((i * NW + w) * kWave + lane) * 16);
+    // max |v| of the bf16 values; with GELU_PRE taken on the fp32 GELU values
+    // before their rounding and rounded once (round-to-nearest is monotonic
+    // and odd, so this is the max of the rounded values)
     float amax = 0.0f;
 #pragma unroll
     for (int i = 0; i < C; ++i)
@@ -86,12 +89,13 @@ __global__ void __launch_bounds__(NW * 64) quantize_rows_wg_kernel(const __bf16*
         for (int e = 0; e < 4; ++e) {
             float lo = bf_lo(buf[i][e]), hi = bf_hi(buf[i][e]);
             if constexpr (GELU_PRE) {
-                buf[i][e] = bf_pack(gelu_tanh_fast(lo), gelu_tanh_fast(hi));
-                lo = bf_lo(buf[i][e]);
-                hi = bf_hi(buf[i][e]);
+                lo = gelu_tanh_fast(lo);
+                hi = gelu_tanh_fast(hi);
+                buf[i][e] = bf_pack(lo, hi);
             }
             amax = fmaxf(amax, fmaxf(fabsf(lo), fabsf(hi)));
         }
+    if constexpr (GELU_PRE) amax = (float)to_bf16(amax);
 #pragma unroll
     for (int i = 0; i < C; ++i) opaque(buf[i]);
     if (GELU_PRE && g_out != nullptr) {
