@@ -399,18 +399,20 @@ __device__ __forceinline__ void tile_origin(int tau, int tiles_m, int tiles_n, i
     n0 = (int64_t)((tau % per_group) / gsize) * L_BN;
 }
 
-// One 256 x 256 tile, K steps [ks0, ks0 + nk) (ks0 and nk even: whole stages), by the whole workgroup: with
-// part == NULL the epilogue writes the outputs, else the int32 sums go to the
-// 256 x 256 row-major partial tile at part.
+// One 256 x 256 tile (TS = 1) or 128 x 128 sub-tile (TS = 2, whole K loop, no
+// partial sums), K steps [ks0, ks0 + nk) (ks0 and nk even: whole stages), by
+// the whole workgroup: with part == NULL the epilogue writes the outputs, else
+// the int32 sums go to the 256 x 256 partial tile at part (fragment order).
 // WN: waves along N (4: 2 x 4 waves of 128 x 64; 2: 4 x 2 waves of 64 x 128,
 // so that one wave holds whole 128-column heads for the fused QKV epilogue).
-// Either way a wave reads 12 fragments per step and issues 32 MFMAs.
+// Either way a wave of a whole tile reads 12 fragments per step and issues 32
+// MFMAs; on a sub-tile (WN = 4, waves of 64 x 32) 6 and 8.
 // W4 (bf16 A only): W holds MXFP4 codes [N, K/2] (E2M1, element 2i in the low
 // nibble of byte i) with E8M0 scales ep.w_mx_scale [N, K/32]; each stage's W
 // tile is decoded to bf16 in registers (hardware fp4 -> bf16 conversion with
 // the fp32 scale) and written to the LDS slot, so 4.25 bits per weight come
 // from memory.  Thread t decodes 32 values: row t/2, K half t%2 of the stage.
-template <bool I8, int EV, int WN, bool W4 = false>
+template <bool I8, int EV, int WN, bool W4 = false, int TS = 1>
 __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_t lda_b,
                                            const uint8_t* __restrict__ W, int64_t M, int64_t N, int64_t Kb,
                                            const EpiParams& ep, uint8_t* lds, int64_t m0, int64_t n0, int ks0,
@@ -419,8 +421,12 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     const int lane = tid % kWave, wave = tid / kWave;
     static_assert(WN == 4 || WN == 2, "wave grid");
     static_assert(!(W4 && I8), "MXFP4 weights go with bf16 activations");
-    static_assert(EV != EV_QKV || WN == 2, "the fused QKV epilogue needs whole heads per wave");
-    constexpr int WTM = L_BM / (8 / WN), WTN = L_BN / WN;   // wave tile
+    static_assert(TS == 1 || (TS == 2 && !W4), "128 x 128 sub-tiles, no MXFP4");
+    constexpr int T_BM = L_BM / TS, T_BN = L_BN / TS;       // tile
+    constexpr int A_BYTES = T_BM * L_SK, STAGE_BYTES = (T_BM + T_BN) * L_SK;
+    constexpr int NLD = 4 / TS;                             // 1 KB loads per wave, operand and stage
+    constexpr int WTM = T_BM / (8 / WN), WTN = T_BN / WN;   // wave tile
+    static_assert(EV != EV_QKV || WTN == 128, "the fused QKV epilogue needs whole heads per wave");
     constexpr int MF = WTM / 16, NF = WTN / 16;             // 16 x 16 accumulator tiles
     const int wm = wave / WN, wn = wave % WN;
 
@@ -436,10 +442,10 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     const __amdgpu_buffer_rsrc_t rs_a = __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, (int)(M * lda_b), 0x00020000);
     const __amdgpu_buffer_rsrc_t rs_w =
         __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(W4 ? N * (Kb / 4) : N * Kb), 0x00020000);
-    int aoff[4], boff[4];
+    int aoff[4], boff[4];   // entries [0, NLD)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int p = (wave * 4 + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
+    for (int i = 0; i < NLD; ++i) {
+        const int p = (wave * NLD + i) * 64 + lane, r = p >> 3, c = (p & 7) ^ (r & 7);
         aoff[i] = (int)(min(m0 + r, M - 1) * lda_b) + c * 16;
         boff[i] = (int)(min(n0 + r, N - 1) * Kb) + c * 16;
     }
@@ -455,11 +461,11 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
         const int64_t gr = min(n0 + row, N - 1);
         w4_off = (int)(gr * (Kb / 4)) + half * 16;
         s4_off = (int)(gr * (Kb / 64)) + half;
-        w4_lds = L_TILE_BYTES + row * L_SK;
+        w4_lds = A_BYTES + row * L_SK;
         w4_sw = (row & 7) | (half << 5);   // chunk c = 4 half + j sits at slot c ^ (row & 7)
         (void)boff;
     }
-    const int wbase = __builtin_amdgcn_readfirstlane(wave * 4 * 1024);
+    const int wbase = __builtin_amdgcn_readfirstlane(wave * NLD * 1024);
     typedef typename std::conditional<I8, v4i, v4f>::type acc_t;
     typedef typename std::conditional<I8, v4i, v8bf>::type frag_t;
     // fragment reads: lane reads chunk (4h + lane / 16) of rows base + lane % 16
@@ -467,18 +473,18 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     const int sw = lane & 7, chunk = lane / 16;
     const int arow = wm * WTM + lane % 16, brow = wn * WTN + lane % 16;
     const int aswz0 = arow * L_SK + ((chunk ^ sw) << 4), aswz1 = arow * L_SK + (((4 + chunk) ^ sw) << 4);
-    const int bswz0 = L_TILE_BYTES + brow * L_SK + ((chunk ^ sw) << 4);
-    const int bswz1 = L_TILE_BYTES + brow * L_SK + (((4 + chunk) ^ sw) << 4);
+    const int bswz0 = A_BYTES + brow * L_SK + ((chunk ^ sw) << 4);
+    const int bswz1 = A_BYTES + brow * L_SK + (((4 + chunk) ^ sw) << 4);
     const int nst = nk / 2;   // stages (nk is even)
 
 #define LG_DMA(stage)                                                                         \
     do {                                                                                      \
         const int kb0 = ks0 * L_BK + (stage) * L_SK;                                          \
-        uint8_t* sl = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES + wbase;                       \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
+        uint8_t* sl = lds + ((stage) % L_SLOTS) * STAGE_BYTES + wbase;                         \
+        _Pragma("unroll") for (int i = 0; i < NLD; ++i) {                                     \
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_a, (lds_ptr_t)(sl + i * 1024), 16, aoff[i], kb0, 0, 0); \
             if constexpr (!W4)                                                                \
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + L_TILE_BYTES + i * 1024), 16, \
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_w, (lds_ptr_t)(sl + A_BYTES + i * 1024), 16, \
                                                          boff[i], kb0, 0, 0);                 \
         }                                                                                     \
     } while (0)
@@ -492,7 +498,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     } while (0)
 #define W4_STORE(stage)                                                                       \
     do {                                                                                      \
-        uint8_t* sl = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES + w4_lds;                      \
+        uint8_t* sl = lds + ((stage) % L_SLOTS) * STAGE_BYTES + w4_lds;                        \
         const float sc = w4_scale == 255u ? __builtin_nanf("") : ldexpf(1.0f, (int)w4_scale - 127); \
         _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                       \
             const uint32_t word = (uint32_t)w4_codes[j];                                      \
@@ -508,7 +514,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 // fragments of step half H of the stage in slot (stage % 2)
 #define LG_FRAGS(stage, H, fa, fb)                                                      \
     do {                                                                                \
-        const uint8_t* src = lds + ((stage) % L_SLOTS) * L_STAGE_BYTES;                 \
+        const uint8_t* src = lds + ((stage) % L_SLOTS) * STAGE_BYTES;                   \
         _Pragma("unroll") for (int j = 0; j < NF; ++j)                                  \
             fb[j] = *reinterpret_cast<const frag_t*>(src + ((H) ? bswz1 : bswz0) + j * 16 * L_SK); \
         _Pragma("unroll") for (int i = 0; i < MF; ++i)                                  \
@@ -536,10 +542,12 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 // interleave: per 8 MFMAs, 3 fragment reads (and 2 loads into LDS when the
 // step issues a stage)
 #define LG_SCHEDULE(LOADS)                                                 \
-    _Pragma("unroll") for (int q = 0; q < 4; ++q) {                        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);                 \
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);                 \
-        if (LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);      \
+    if constexpr (TS == 1) {                                               \
+        _Pragma("unroll") for (int q = 0; q < 4; ++q) {                    \
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);             \
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);             \
+            if (LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  \
+        }                                                                  \
     }
 // stage s: step 2s (fragments of step 2s+1), then step 2s+1 (loads of stage
 // s+2 when LOADS, fragments of step 2s+2).  One barrier per stage, after step
@@ -641,8 +649,12 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     } else {
         LG_DMA(0);
         if (nst > 1) {
+            // this wave's loads of stage 1 (2 NLD) may stay in flight
             LG_DMA(1);
-            LG_BARRIER(8);
+            if constexpr (TS == 1)
+                LG_BARRIER(8);
+            else
+                LG_BARRIER(4);
         } else {
             LG_BARRIER(0);
         }
@@ -677,7 +689,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
 #undef LG_SCHEDULE
 #undef LG_PAIR
 
-    if (part != nullptr) {
+    if (TS == 1 && part != nullptr) {
         // K-split partial sums go straight from the accumulators, in fragment
         // order: 16-byte piece ((((wm MF + i) WN + wn) NF + j) 64 + lane) holds
         // acc[i][j], so each store of a wave is 1 KB contiguous and the 16 KB
@@ -699,6 +711,8 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     // columns of one row (LPR lanes per row, RPP rows per pass).
     constexpr int EP_STRIDE = WTN + 4;   // words per slab row (padded)
     constexpr int LPR = WTN / 16, RPP = kWave / LPR;
+    // rows of a slab per pass: RPP (lanes of rows past the slab's 16 idle)
+    constexpr int PASSES = RPP >= 16 ? 1 : 16 / RPP;
     static_assert(2 * 8 * 16 * EP_STRIDE * 4 <= L_CONST, "slab buffers");
     float* const slab_buf[2] = {reinterpret_cast<float*>(lds) + wave * 16 * EP_STRIDE,
                                 reinterpret_cast<float*>(lds) + (8 + wave) * 16 * EP_STRIDE};
@@ -740,8 +754,8 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     for (int i = 0; i < MF; ++i) {
         const float* slab = slab_buf[i & 1];
 #pragma unroll
-        for (int pass = 0; pass < 16 / RPP; ++pass) {
-            const int er = pass * RPP + er0;
+        for (int pass = 0; pass < PASSES; ++pass) {
+            const int er = min(pass * RPP + er0, 15);
             const int64_t m = m0 + wm * WTM + i * 16 + er;
             // this row's 16 accumulators (and its activation scale) first, then
             // slab i+1 is parked while they are finished: a wave's LDS accesses
@@ -757,7 +771,7 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
             }
             float v[16];
             int32_t ai[16];
-            const bool ok = m < M && n < N;
+            const bool ok = pass * RPP + er0 < 16 && m < M && n < N;
             if (ok) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
@@ -805,7 +819,11 @@ __device__ __forceinline__ void large_tile(const uint8_t* __restrict__ A, int64_
     asm volatile("" ::: "memory");
 }
 
-template <bool I8, int EV, int WN, bool W4 = false>
+// SUB > 0: the r tiles of the last round are not split along K but into
+// SUB x SUB sub-tiles of (256 / SUB)^2 with the whole K loop each (S = SUB^2
+// jobs per tile): no partial sums and no reduce, at the price of smaller
+// tiles (more operand bytes and fragment reads per product) for that round.
+template <bool I8, int EV, int WN, bool W4 = false, int SUB = 0>
 __global__ void __launch_bounds__(L_THREADS, 1)
 gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* __restrict__ W,
                   int64_t M, int64_t N, int64_t Kb, EpiParams ep, LargePlan lp) {
@@ -842,6 +860,15 @@ gemm_large_kernel(const uint8_t* __restrict__ A, int64_t lda_b, const uint8_t* _
             const int rS = lp.r * lp.S, x = b % 8, q = rS / 8, rem = rS % 8;
             const int J = x * q + min(x, rem) + b / 8;
             const int t = J / lp.S, k = J % lp.S;
+            if constexpr (SUB > 0) {
+                // sub-tile k of tile t: rows (k / SUB) 256/SUB.., columns (k % SUB) 256/SUB..
+                int64_t m0, n0;
+                tile_origin(lp.tail0 + t, tiles_m, tiles_n, m0, n0);
+                m0 += (int64_t)(k / SUB) * (L_BM / SUB);
+                n0 += (int64_t)(k % SUB) * (L_BN / SUB);
+                large_tile<I8, EV, 4, false, SUB>(A, lda_b, W, M, N, Kb, ep, lds, m0, n0, 0, nk_all, nullptr);
+                continue;
+            }
             // whole 128-byte stages
             ks0 = 2 * (int)((int64_t)k * (nk_all / 2) / lp.S);
             nk = 2 * (int)((int64_t)(k + 1) * (nk_all / 2) / lp.S) - ks0;
@@ -1016,38 +1043,71 @@ bool gemm_bf16_direct_mxfp4(int64_t M, int64_t N, int64_t K, int64_t lda, bool c
     return takes_large(M, N, lda * 2, K * 2, can_split);
 }
 
+// One persistent launch (two for long K loops with a split remainder) of the
+// 256 x 256 kernel: full whole tiles, then r remainder tiles as S jobs each
+// (K ranges with SUB == 0, sub-tiles otherwise).
+template <bool I8, int EV, bool W4, int SUB>
+static void launch_large(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
+                         const EpiParams& ep, hipStream_t st, int64_t tiles, int64_t full, int32_t r, int S) {
+    constexpr int kWN = EV == EV_QKV ? 2 : 4;
+    static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
+    if (!lds_set) {
+        (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN, W4, SUB>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
+        lds_set = true;
+    }
+    const int C = num_cus();
+    if (S && Kb / L_BK > 64) {
+        // long K loops: whole tiles, then the jobs of the remainder tiles
+        if (full > 0)
+            gemm_large_kernel<I8, EV, kWN, W4, SUB><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
+                a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
+        gemm_large_kernel<I8, EV, kWN, W4, SUB><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
+            a, lda_b, w, M, N, Kb, ep, LargePlan{0, (int32_t)full, r, S});
+    } else {
+        // persistent: at most one workgroup per compute unit, and one for
+        // each remainder job (r * S <= C)
+        const int64_t G = std::min<int64_t>(C, std::max<int64_t>(full > 0 ? tiles : 0, (int64_t)r * S));
+        gemm_large_kernel<I8, EV, kWN, W4, SUB><<<(unsigned)(G > 0 ? G : std::min<int64_t>(C, tiles)), L_THREADS,
+                                                  L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
+                                                               LargePlan{(int32_t)full, (int32_t)full, r, S});
+    }
+    if (SUB == 0 && S) split_reduce_kernel<I8, EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
+}
+
+// Sub-tiles for the r tiles of a partial last round after at least one whole
+// round: 128 x 128 (4 jobs per tile) when that gives between C/2 and C jobs,
+// else 0 (K-split, or a plain partial round).  Measured on the 1024px block
+// (same-process A/B against the K-split): MLP up (r = 64) 253.7 -> 244.1 us;
+// 64 x 64 sub-tiles for out / down (r = 16) were 12 and 34 us slower, and the
+// QKV epilogue's 8 x 1 wave grid on 128 x 128 sub-tiles 13 us slower (one A
+// and eight B fragment reads per eight MFMAs).
+static int remainder_subtiles(int64_t tiles, int ev, bool w4) {
+    const int64_t C = num_cus(), R = tiles / C, r = tiles - R * C;
+    if (w4 || ev == EV_QKV || R < 1 || r == 0) return 0;
+    return 4 * r <= C && 8 * r >= C ? 2 : 0;
+}
+
 template <bool I8, int EV, bool W4 = false>
 static void launch_mfma(const uint8_t* a, int64_t lda_b, const uint8_t* w, int64_t M, int64_t N, int64_t Kb,
                         const EpiParams& ep, hipStream_t st) {
-    constexpr int kWN = EV == EV_QKV ? 2 : 4;
     if (W4 || takes_large(M, N, lda_b, Kb, ep.split_partial != nullptr)) {
-        static bool lds_set = false;   // allow 128 KB of dynamic LDS (once per instantiation)
-        if (!lds_set) {
-            (void)hipFuncSetAttribute((const void*)gemm_large_kernel<I8, EV, kWN, W4>,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)L_LDS);
-            lds_set = true;
-        }
         const int64_t tiles = large_grid(M, N);
+        const int sub = remainder_subtiles(tiles, EV, W4);
+        if constexpr (!W4) {
+            if constexpr (EV != EV_QKV) {
+                if (sub) {
+                    const int64_t full = tiles / num_cus() * num_cus();
+                    launch_large<I8, EV, W4, 2>(a, lda_b, w, M, N, Kb, ep, st, tiles, full, (int32_t)(tiles - full),
+                                                4);
+                    return;
+                }
+            }
+        }
         int64_t full = tiles;
         const int S = plan_split(tiles, (int)(Kb / L_BK), ep, &full);
         const int32_t r = S ? (int32_t)(tiles - full) : 0;
-        const int C = num_cus();
-        if (S && Kb / L_BK > 64) {
-            // long K loops: whole tiles, then the K ranges of the split tiles
-            if (full > 0)
-                gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)std::min<int64_t>(C, full), L_THREADS, L_LDS, st>>>(
-                    a, lda_b, w, M, N, Kb, ep, LargePlan{(int32_t)full, (int32_t)full, 0, 0});
-            gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)(r * S), L_THREADS, L_LDS, st>>>(
-                a, lda_b, w, M, N, Kb, ep, LargePlan{0, (int32_t)full, r, S});
-        } else {
-            // persistent: at most one workgroup per compute unit, and one for
-            // each split range (r * S <= C)
-            const int64_t G = std::min<int64_t>(C, std::max<int64_t>(full > 0 ? tiles : 0, (int64_t)r * S));
-            gemm_large_kernel<I8, EV, kWN, W4><<<(unsigned)(G > 0 ? G : std::min<int64_t>(C, tiles)), L_THREADS,
-                                                 L_LDS, st>>>(a, lda_b, w, M, N, Kb, ep,
-                                                              LargePlan{(int32_t)full, (int32_t)full, r, S});
-        }
-        if (S) split_reduce_kernel<I8, EV><<<(unsigned)(r * 16), 256, 0, st>>>(M, N, ep, (int32_t)full, S);
+        launch_large<I8, EV, W4, 0>(a, lda_b, w, M, N, Kb, ep, st, tiles, full, r, S);
     }
     else if constexpr (EV == EV_QKV) {
         // store the QKV output, then the separate norm/RoPE kernel

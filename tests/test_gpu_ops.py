@@ -70,12 +70,14 @@ def test_quantize_outlier_weights_bit_exact():
                                       (4352, 4096, 1024, True), (4429, 4144, 2048, True),
                                       (1024, 15360, 256, False), (1152, 3072, 4096, True),
                                       (1152, 1536, 8192, True), (320, 12288, 4096, True),
-                                      (320, 4096, 16384, True)])
+                                      (320, 4096, 16384, True), (4352, 16384, 256, True)])
 def test_w8a8_linear_exact_accumulators(M, N, K, ws):
-    """ws=True passes a workspace: tiles of a partial last round (272 / 306 tiles on
-    256 CUs), or every tile of a launch with fewer tiles than CUs (60 and 30 tiles,
-    the second with a long K loop), are split along K and their partial int32 sums
+    """ws=True passes a workspace: tiles of a partial last round (272 tiles on 256
+    CUs), or every tile of a launch with fewer tiles than CUs (60 and 30 tiles, the
+    second with a long K loop), are split along K and their partial int32 sums
     added by a reduce launch; 240 tiles without a workspace run as one partial round.
+    A last round of 32..64 tiles (306 tiles at 4429 x 4144 with ragged edges, 1088
+    at 4352 x 16384) runs as 128 x 128 sub-tiles with the whole K loop instead.
     At M = 320 the second row of tiles holds 64 rows (its partial sums store only
     those), with a short (96 tiles) and a long (32 tiles) K loop."""
     say("w8a8", M, N, K, ws)
