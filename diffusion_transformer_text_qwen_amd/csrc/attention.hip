@@ -52,10 +52,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t kv_rsrc(const __bf16* base, in
 }
 
 // Software pipeline over key tiles.  K and V have separate double buffers, K
-// one tile ahead: while the VALU turns the scores of tile t into P, the MFMA
-// pipe computes the scores of tile t+1; then P V of tile t runs while tile
-// t+2's K and tile t+1's V go from registers to LDS and the global loads of
-// the next ones are issued.  One barrier per tile.
+// one tile ahead: while the MFMA pipe computes the scores of tile t+1, the
+// VALU turns the first half of tile t's scores into P (and tile t+2's K goes
+// from registers to LDS, tile t+3's K is loaded); then P V of tile t runs,
+// its first half beside P of the second key half, its second half while tile
+// t+1's V goes from registers to LDS; tile t+2's V is loaded last.  One
+// barrier per tile.
 __global__ void __launch_bounds__(256, 2)
 attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
                  const __bf16* __restrict__ Vg, __bf16* __restrict__ O, int T_q, int T_k,
@@ -152,7 +154,7 @@ attn_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ Kg,
     float m_run = -INFINITY, l_run = 0.0f;
 
     // One pipeline step: softmax of tile t (scores in scur) overlapped with
-    // the scores of tile t+1 (into snxt, from knext); then P V of tile t from
+    // the scores of tile t+1 (into snxt, from knext) and P V of tile t from
     // vcur; stores K(t+2) into kfree and V(t+1) into vnext; loads K(t+3),
     // V(t+2).  Buffers past the last tile hold zeros or unused keys.
     auto step = [&](int t, v16f(&scur)[2], v16f(&snxt)[2], const uint8_t* knext, const uint8_t* vcur,
