@@ -1200,13 +1200,19 @@ int dit_velocity_forward(const dit_block_config* cfg, const dit_block_weights* b
     s = check_io(cfg, &bio);
     if (s) return s;
     hipStream_t st = S(stream);
-    // y[M, Nn] = a[M, K] w[Nn, K]^T + b in the activation dtype
+    // y[M, Nn] = a[M, K] w[Nn, K]^T + b in the activation dtype.  The bf16
+    // linears of the head and tail use the blocks' K-split region (free
+    // outside the blocks), so launches with few tiles (txt_in on the text
+    // rows, proj_out's 64 columns) split along K instead of running on a few CUs.
+    int32_t* head_split = f32 ? nullptr : (int32_t*)(blk + plan(cfg, T_q, T_k).split);
     auto linear = [&](const void* a, int64_t M, int64_t K, const void* w, const float* b, void* y,
                       int64_t Nn) -> hipError_t {
         if (M == 0) return hipSuccess;
         EpiParams ep = store_epi(y, Nn, !f32, b);
-        return f32 ? launch_gemm_f32((const float*)a, K, (const float*)w, M, Nn, K, ep, st)
-                   : launch_gemm_bf16(a, K, w, M, Nn, K, ep, st);
+        if (f32) return launch_gemm_f32((const float*)a, K, (const float*)w, M, Nn, K, ep, st);
+        ep.split_partial = head_split;
+        ep.split_bytes = kSplitPartialBytes;
+        return launch_gemm_bf16(a, K, w, M, Nn, K, ep, st);
     };
     // latent rows -> activation dtype (the fp32 mode reads the fp32 latent directly)
     auto lat_rows = [&](const float* src, int64_t rows, uint8_t* dst) -> const void* {
